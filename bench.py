@@ -1,0 +1,293 @@
+"""Benchmark of the RPTQ hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  1. fused LayerNorm + reorder + per-cluster quantize (4-bit), OPT-66B fc1
+     input: 16384 tokens (batch 8 x seq 2048) x 9216 channels, g = 32;
+  2. cluster-segmented int8-MFMA GEMM 9216 -> 36864 on those codes (W4A4);
+  3. + 4. the same pair with 3-bit activations (W4A3);
+  5. K/V cache quantize + pack, 3-bit, g = 32, of K and of V, each
+     [64 x 8192 tokens][72 heads x 128] fp16 (OPT-66B KV cache);
+  6. K/V dequantize of both back to fp16.
+Inputs are generated (seeded, synthetic) and resident in HBM before the timed
+region.  `value` is the tokens/s of the W4A4 LayerNorm-quant -> GEMM pair,
+tokens / (t_LN + t_GEMM), with kernel times from HIP events recorded on the
+stream the kernels are launched on; the other kernels' rates are extra keys.
+`--gpus N` with N > 1 is refused: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA (5.0 POPS)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "qgemm": ["post_quantization_layernorm_amd/csrc/qgemm.hip"],
+    "ln_reorder_quant": ["post_quantization_layernorm_amd/csrc/ln_quant.hip",
+                         "post_quantization_layernorm_amd/csrc/rptq_device.hpp"],
+    "kv_quant_pack": ["post_quantization_layernorm_amd/csrc/kv.hip",
+                      "post_quantization_layernorm_amd/csrc/rptq_device.hpp"],
+}
+
+
+def measured_traffic(kernel: str, launches_bytes: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path)).get(kernel)
+    if not d or d.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-kv", action="store_true", help="skip the K/V cache kernels (profiling runs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: every box in this setup has a single MI355X and the "
+              "library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import post_quantization_layernorm_amd as P
+    import synthetic
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    t_setup = time.time()
+
+    # ------------------------------------------------------------------ OPT-66B fc1 layer
+    w = synthetic.WORKLOADS["opt66b_fc1_w4a4"]
+    M, K, N, g = w.M, w.K, w.N, w.g
+    mu, sg = synthetic.channel_params(K, w.seed, w.outlier_frac)
+    gamma, beta = synthetic.ln_params(K, w.seed, random=False)         # LayerNorm default init
+    g_d = torch.from_numpy(gamma).to(dev); b_d = torch.from_numpy(beta).to(dev)
+    xc = torch.from_numpy(synthetic.tokens(w.calib_tokens, mu, sg, w.seed, synthetic.STREAM_CALIB)).to(dev)
+    mx, mn = P.rptq_calib_minmax(xc, P.RPTQ_IN_FP16_RAW, g_d, b_d)
+    mx, mn = mx.cpu().numpy(), mn.cpu().numpy()
+    R, bounds = P.rptq_kmeans_reorder(mx, mn, g, synthetic.kmeans_uniforms(w.seed, 10, g), n_init=10)
+    R_d = torch.from_numpy(R).to(dev)
+    gr_d = g_d[R_d].contiguous(); br_d = b_d[R_d].contiguous()
+    x = torch.from_numpy(synthetic.tokens(M, mu, sg, w.seed, synthetic.STREAM_EVAL)).to(dev)
+    log(f"[bench] layer inputs ready ({time.time() - t_setup:.1f}s)")
+    W = synthetic.weights(K, N, w.seed)
+    wq, s_w = P.rptq_quantize_weights(W, w.w_bits)
+    del W
+    wp, cs = P.rptq_pack_weights(wq, R, bounds, w.w_bits)
+    del wq
+    wp_d = torch.from_numpy(wp).to(dev); cs_d = torch.from_numpy(cs).to(dev)
+    sw_d = torch.from_numpy(s_w).to(dev)
+    del wp
+    variants = {}
+    for ab in (4, 3):
+        s, z = P.rptq_cluster_params(mx, mn, R, bounds, ab)
+        rb = P.rptq_codes_row_bytes(bounds, ab)
+        variants[ab] = dict(s=s, z=z, codes=torch.empty((M, rb), dtype=torch.uint8, device=dev))
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    kpad = P.rptq_codes_kpad(bounds)
+    log(f"[bench] weights ready, K_pad={kpad} ({time.time() - t_setup:.1f}s)")
+
+    # ------------------------------------------------------------------ OPT-66B KV cache
+    kvw = synthetic.KV_WORKLOADS["opt66b_kv_a3"]
+    T, C, kvb = kvw.T, kvw.C, kvw.bits
+    kv = {}
+    if not args.no_kv:
+        for name, (s_ch, s_cal, s_ev) in {"K": (synthetic.STREAM_CHANNELS, synthetic.STREAM_CALIB,
+                                                synthetic.STREAM_EVAL),
+                                          "V": (synthetic.STREAM_CHANNELS_V, synthetic.STREAM_CALIB_V,
+                                                synthetic.STREAM_EVAL_V)}.items():
+            kmu, ksg = synthetic.channel_params(C, kvw.seed, kvw.outlier_frac, stream=s_ch)
+            kc = torch.from_numpy(synthetic.tokens(kvw.calib_tokens, kmu, ksg, kvw.seed, s_cal)).to(dev)
+            kmx, kmn = P.rptq_calib_minmax(kc, P.RPTQ_CALIB_RAW)
+            kmx, kmn = kmx.cpu().numpy(), kmn.cpu().numpy()
+            kR, kbnd = P.rptq_kmeans_reorder(kmx, kmn, kvw.g, synthetic.kmeans_uniforms(kvw.seed + len(name), 10,
+                                                                                      kvw.g), n_init=10)
+            ks, kz = P.rptq_cluster_params(kmx, kmn, kR, kbnd, kvb)
+            data = synthetic.tokens_device(T, kmu, ksg, kvw.seed, s_ev)
+            kv[name] = dict(x=data, R=torch.from_numpy(kR).to(dev), bounds=kbnd, s=ks, z=kz,
+                            packed=torch.empty((T, P.rptq_kv_row_bytes(C, kvb)), dtype=torch.uint8, device=dev),
+                            out=torch.empty((T, C), dtype=torch.float16, device=dev))
+        log(f"[bench] KV caches ready ({time.time() - t_setup:.1f}s)")
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------ one step
+    names = ["ln4", "gemm4", "ln3", "gemm3"] + ([] if args.no_kv else ["kvq_K", "kvq_V", "kvd_K", "kvd_V"])
+
+    def step(ev=None):
+        def rec(i):
+            if ev is not None:
+                ev[i].record(stream)
+        k = 0
+        for ab in (4, 3):
+            v = variants[ab]
+            rec(k)
+            P.rptq_ln_reorder_quant(x, R_d, gr_d, br_d, bounds, v["s"], v["z"], ab, out=v["codes"], stream=stream)
+            rec(k + 1)
+            P.rptq_qgemm(v["codes"], M, K, N, bounds, v["s"], v["z"], ab, wp_d, w.w_bits, sw_d, cs_d, out=Y,
+                         stream=stream)
+            k += 2
+        rec(k)
+        if not args.no_kv:
+            for name in ("K", "V"):
+                d = kv[name]
+                P.rptq_kv_quant_pack(d["x"], d["R"], d["bounds"], d["s"], d["z"], kvb, out=d["packed"], stream=stream)
+                k += 1
+                rec(k)
+            for name in ("K", "V"):
+                d = kv[name]
+                P.rptq_kv_dequant(d["packed"], C, d["R"], d["bounds"], d["s"], d["z"], kvb, out=d["out"],
+                                  stream=stream)
+                k += 1
+                rec(k)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({time.time() - t_setup:.1f}s)")
+
+    nev = len(names) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)      # seconds
+    avg = {n: float(np.mean(v)) for n, v in per.items()}
+    log("[bench] per-kernel avg ms: " + ", ".join(f"{n}={avg[n] * 1e3:.3f}" for n in names))
+
+    ops = 2.0 * M * N * K
+    res_layer = {}
+    for ab in (4, 3):
+        t_ln, t_gm = avg[f"ln{ab}"], avg[f"gemm{ab}"]
+        ln_bytes = M * K * (2 + ab / 8)
+        res_layer[ab] = dict(tokens_per_s=M / (t_ln + t_gm), ln_ms=t_ln * 1e3, gemm_ms=t_gm * 1e3,
+                             gemm_tops=ops / t_gm / 1e12, gemm_frac_int8_peak=ops / t_gm / 1e12 / INT8_PEAK_TOPS,
+                             ln_GBps=ln_bytes / t_ln / 1e9, ln_frac_hbm_peak=ln_bytes / t_ln / 1e9 / HBM_PEAK_GBPS)
+    out = {}
+    if not args.no_kv:
+        kv_bytes = T * C * (2 + kvb / 8)
+        tq = (avg["kvq_K"] + avg["kvq_V"]) / 2
+        td = (avg["kvd_K"] + avg["kvd_V"]) / 2
+        out["kv_pack_GBps"] = kv_bytes / tq / 1e9
+        out["kv_pack_frac_hbm_peak"] = kv_bytes / tq / 1e9 / HBM_PEAK_GBPS
+        out["kv_dequant_GBps"] = kv_bytes / td / 1e9
+        out["kv_pack_ms"] = tq * 1e3
+        out["kv_dequant_ms"] = td * 1e3
+
+    gemm_ops_launch = ops
+    t_gemm = avg["gemm4"]
+    traffic = measured_traffic("qgemm", gemm_ops_launch)
+    roofline = {"bound": "mfma", "achieved": ops / t_gemm / 1e12, "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": ops / t_gemm / 1e12 / INT8_PEAK_TOPS, "traffic": traffic,
+                "kernel": "qgemm_kernel<4,4>", "work_per_launch": f"2*M*N*K = {ops:.4g} int8 ops (unpadded K)"}
+    ln_bytes = M * K * (2 + 4 / 8)
+    rooflines = [roofline,
+                 {"bound": "hbm", "kernel": "ln_reorder_quant_kernel<4,0>", "achieved": ln_bytes / avg["ln4"] / 1e9,
+                  "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ln_bytes / avg["ln4"] / 1e9 / HBM_PEAK_GBPS,
+                  "traffic": measured_traffic("ln_reorder_quant", ln_bytes)}]
+    if not args.no_kv:
+        rooflines.append({"bound": "hbm", "kernel": "kv_quant_pack_kernel<3>", "achieved": out["kv_pack_GBps"],
+                          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": out["kv_pack_frac_hbm_peak"],
+                          "traffic": measured_traffic("kv_quant_pack", T * C * (2 + kvb / 8))})
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, x, gamma, beta, R, bounds, variants[4]["s"], variants[4]["z"], N, args.cpu_seconds)
+
+    line = {
+        "metric": "tokens/s + TOPS of fused LN-quant->qGEMM (% int8 MFMA peak); KV-pack GB/s",
+        "value": res_layer[4]["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8 MFMA (u4/u3 activation codes, s4 weights), fp32 LN/epilogue",
+        "data": "synthetic (seeded per-channel N(mu_c, sigma_c) activations with 1% x100 outlier channels; "
+                "W ~ N(0, 0.02))",
+        "config": {"workload": "OPT-66B fc1 layer W4A4 (+W4A3): LayerNorm(9216)+per-cluster quant -> "
+                               "9216x36864 GEMM, 16384 tokens, g=32; plus OPT-66B KV cache 3-bit, "
+                               "2 x [524288 x 9216] fp16",
+                   "M": M, "K": K, "N": N, "g": g, "K_pad": kpad, "tokens_per_step": M},
+        "tops": res_layer[4]["gemm_tops"],
+        "gemm_frac_int8_peak": res_layer[4]["gemm_frac_int8_peak"],
+        "ln_quant_GBps": res_layer[4]["ln_GBps"],
+        "ln_quant_frac_hbm_peak": res_layer[4]["ln_frac_hbm_peak"],
+        "w4a3": res_layer[3],
+        "w4a4": res_layer[4],
+        **out,
+        "per_kernel_ms": {n: avg[n] * 1e3 for n in names},
+        "roofline": roofline,
+        "rooflines": rooflines,
+        "cpu_baseline": cpu,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, x_dev, gamma, beta, R, bounds, s, z, N, budget_s):
+    """The oracle (plain C++/OpenMP, never tuned) on a bounded row sample of
+    the same layer: LayerNorm + reorder + quantize + pack, then the
+    segmented integer GEMM with its epilogue.  Rows are added until about
+    `budget_s` seconds of CPU work."""
+    import oracle as orc
+    import synthetic
+    rows_x = x_dev[:64].cpu().numpy()
+    W = synthetic.weights(w.K, N, w.seed)
+    Wq, s_w = orc.quantize_weights(W, w.w_bits)
+    del W
+    done, t_tot = 0, 0.0
+    chunk = 8
+    while t_tot < budget_s and done + chunk <= rows_x.shape[0]:
+        xs = rows_x[done:done + chunk]
+        t0 = time.perf_counter()
+        codes = orc.ln_reorder_quant(xs, gamma, beta, 1e-5, R, bounds, s, z, 4)
+        q = orc.unpack_seg32(codes, w.K, bounds, 4)
+        orc.qgemm(q, Wq, R, bounds, s, z, s_w)
+        t_tot += time.perf_counter() - t0
+        done += chunk
+    return {"value": done / t_tot, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"{done} of {w.M} tokens of the W4A4 layer (LN+quant+pack+segmented GEMM, N={N})",
+            "seconds": t_tot}
+
+
+if __name__ == "__main__":
+    main()

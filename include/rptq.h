@@ -1,0 +1,264 @@
+/*
+ * rptq.h -- C ABI of the MI355X (gfx950) library for the runtime hot path of
+ * RPTQ, reorder-based post-training quantization of LLM activations.
+ *
+ * Method (RPTQ write-up "基于重排序的新量化方法RPTQ：实现大型语言模型的 3 比特量化",
+ * method section): activation channels are grouped by KMeans on their
+ * calibration (max, min) points into g clusters; a reorder index R places the
+ * channels of a cluster next to each other; every cluster has its own scale s
+ * and zero point z.  Explicit runtime reordering is avoided: LayerNorm emits
+ * the reordered activations directly (gamma/beta taken in R order) and the
+ * rows of the next linear layer's weights are permuted by R offline (Fig. 3).
+ * Quantization follows the uniform asymmetric rule of the quantization
+ * lecture (gitcode.csdn.net, sections 1 and 1.3): W = S (Wq - Z), one (S, Z)
+ * per cluster for activations, symmetric per-output-channel scales for weights.
+ *
+ * Notation.  M tokens (rows), K channels, N output features, g clusters
+ * (1 <= g <= 64), b = activation bits in {3, 4, 8}, qmax = 2^b - 1.
+ *   R[j]       natural channel at reordered position j (int32 [K]).
+ *   bounds     int32 [g+1]; cluster c holds reordered positions
+ *              [bounds[c], bounds[c+1]); bounds[0] = 0, bounds[g] = K,
+ *              strictly increasing.
+ *   s, z       per-cluster scale (fp32 > 0, finite) and zero point (int32,
+ *              |z| <= 2^21).  Not clipped to [0, qmax]: a cluster whose range
+ *              excludes 0 keeps its own range.
+ *
+ * Quantization of a value v in cluster c (every entry point, bit-exact):
+ *   inv_s = 1.0f / s_c                (fp32, correctly rounded, host side)
+ *   q     = clip( rne(v * inv_s) + z_c, 0, qmax )
+ * where v * inv_s is the exact product (fused multiply-add on the device),
+ * rne rounds half to even, and the clip is exact integer arithmetic.  NaN
+ * inputs give an unspecified code; +-inf clip to qmax / 0.
+ *
+ * Code layouts (the pages fix none; these are the library's).  A row of codes
+ * is cut into groups packed independently:
+ *   b = 8: one byte per code.
+ *   b = 4: 8 codes c0..c7 in 4 bytes; byte i (0..3) = c_i | c_(4+i) << 4.
+ *   b = 3: 32 codes c0..c31 in 12 bytes = little-endian words d0, d1, d2; in
+ *          byte i (0..3) of each word:
+ *            d0: bits 0-2 c_i,      bits 3-5 c_(4+i),  bits 6-7 = c_(24+i) & 3
+ *            d1: bits 0-2 c_(8+i),  bits 3-5 c_(12+i), bits 6-7 = c_(28+i) & 3
+ *            d2: bits 0-2 c_(16+i), bits 3-5 c_(20+i), bit 6 = c_(24+i) >> 2,
+ *                                                      bit 7 = c_(28+i) >> 2
+ *   DENSE rows (K/V cache): the row's codes in reordered order, groups back
+ *     to back; row bytes = C * b / 8.
+ *   SEG32 rows (LayerNorm output, GEMM input): cluster c starts at padded
+ *     position off_c = sum_{c'<c} ceil(n_c'/32)*32 (n_c = cluster size) and is
+ *     padded with code 0 up to a multiple of 32; K_pad = off_g; row bytes =
+ *     K_pad * b / 8 (see rptq_codes_row_bytes).
+ *
+ * Conventions for every entry point.
+ *   - Pointers marked "device" are GPU memory owned by the caller (for
+ *     instance torch tensors); they must stay valid until the work queued on
+ *     `stream` has run.  Pointers marked "host" are read before the call
+ *     returns and may be freed afterwards.  The library allocates nothing and
+ *     keeps no state between calls; it is reentrant.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device entry
+ *     points only enqueue work and return; they do not synchronize.
+ *   - Every argument is validated on the host before any HIP call; on error
+ *     nothing is launched.  M = 0 (or T = 0) is a valid no-op.
+ *   - Device pointers must be 16-byte aligned (RPTQ_ERR_ALIGNMENT).
+ *   - Return value: RPTQ_OK or a negative rptq_status; rptq_last_error()
+ *     returns a message for the calling thread's last failure.
+ */
+#ifndef RPTQ_H
+#define RPTQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RPTQ_OK = 0,
+    RPTQ_ERR_INVALID_ARG = -1,   /* bad value, null pointer, inconsistent sizes   */
+    RPTQ_ERR_UNSUPPORTED = -2,   /* valid but outside what the kernels implement  */
+    RPTQ_ERR_ALIGNMENT = -3,     /* device pointer not 16-byte aligned            */
+    RPTQ_ERR_HIP = -4            /* a HIP call or kernel launch failed            */
+} rptq_status;
+
+#define RPTQ_MAX_CLUSTERS 64
+#define RPTQ_MAX_K 16384
+#define RPTQ_MAX_ABS_ZERO_POINT (1 << 21)
+
+enum {
+    RPTQ_IN_FP16_RAW = 0,         /* x: fp16 [M][K], natural channel order: LayerNorm, then quantize */
+    RPTQ_IN_FP32_NORMALIZED = 1   /* x: fp32 [M][K], already normalized, already in R order: quantize only */
+};
+
+/* ---------------------------------------------------------------- hot path */
+
+/*
+ * Fused LayerNorm + reorder + per-cluster quantize + SEG32 pack, one pass
+ * over each row (RPTQ write-up, method section and Fig. 3: LayerNorm emits
+ * the reordered activations, so no explicit reorder pass exists; Houmo
+ * article, RPTQ section: fused, the reorder costs almost nothing).
+ *   in_mode RPTQ_IN_FP16_RAW: per row, mu = mean(x), var = mean((x-mu)^2)
+ *     (biased), y[j] = gamma_r[j] * (x[R[j]] - mu) / sqrt(var + eps) + beta_r[j]
+ *     computed in fp32, then quantized with cluster(j)'s (s, z).
+ *   in_mode RPTQ_IN_FP32_NORMALIZED: y = x (already reordered); quantize only.
+ * x        device, fp16 [M][K] (mode 0) or fp32 [M][K] (mode 1), row-major.
+ * gamma_r, beta_r  device fp32 [K] in R order (gamma[R[j]]); mode 0 only.
+ * eps      > 0, mode 0 only.
+ * R        device int32 [K], a permutation of 0..K-1 (not checked); NULL = identity.
+ *          Mode 0 only.
+ * bounds, s, z   host, as above.  bits in {3, 4, 8}.
+ * codes    device uint8 [M][rptq_codes_row_bytes(bounds, g, bits)], SEG32.
+ * Limits: K % 8 == 0 and K <= RPTQ_MAX_K (RPTQ_ERR_UNSUPPORTED otherwise).
+ */
+int rptq_ln_reorder_quant(const void* x, int32_t in_mode, int64_t M, int32_t K,
+                          const float* gamma_r, const float* beta_r, float eps,
+                          const int32_t* R,
+                          const int32_t* bounds, int32_t g, const float* s, const int32_t* z,
+                          int32_t bits, uint8_t* codes, void* stream);
+
+/*
+ * Cluster-segmented integer GEMM with the zero-point correction folded into
+ * the epilogue (RPTQ write-up, motivation: quantization speeds up matrix
+ * multiplication and linear layers; method / Fig. 3: weights reordered so the
+ * layer consumes the reordered activations).  With W' the reordered,
+ * quantized weights and colsum_c[n] = sum_{j in c} W'[j][n]:
+ *   acc_c[m][n] = sum_{j in c} q[m][j] * W'[j][n]          (int32, exact)
+ *   Y[m][n]     = s_w[n] * sum_c s_c * (acc_c[m][n] - z_c * colsum_c[n])
+ * which is the product of the dequantized activations s_c (q - z_c) and the
+ * dequantized weights s_w[n] W' (quantization lecture 1.3), summed in
+ * reordered order -- exact, because a permutation of the summation index
+ * does not change the sum.
+ * codes    device, SEG32 [M][rptq_codes_row_bytes(bounds, g, a_bits)] (the
+ *          output of rptq_ln_reorder_quant); pad codes must be 0.
+ * K        number of real channels (bounds[g] == K).
+ * bounds, s, z   host; a_bits in {3, 4, 8}.
+ * w_packed device, output of rptq_pack_weights: [N][K_pad] w_bits-bit two's
+ *          complement codes, K contiguous per output feature, grouped like
+ *          the activation codes (w_bits in {4, 8}); pad rows are 0.
+ * s_w      device fp32 [N];  colsum device int32 [g][N].
+ * Y        device fp32 [M][N], row-major.
+ * acc_debug device int32 [g][M][N] or NULL: receives every acc_c (validation).
+ * Limits: N % 8 == 0 (RPTQ_ERR_UNSUPPORTED); every |acc_c| must fit int32
+ * (always true for K <= RPTQ_MAX_K).
+ */
+int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N,
+               const int32_t* bounds, int32_t g, const float* s, const int32_t* z, int32_t a_bits,
+               const uint8_t* w_packed, int32_t w_bits, const float* s_w, const int32_t* colsum,
+               float* Y, int32_t* acc_debug, void* stream);
+
+/*
+ * K/V-cache quantize + pack (RPTQ write-up, evaluation: the KV-cache settings
+ * W4A4KV / W4A3KV / W3A3KV quantize the key and value caches, which hold most
+ * of the memory at large batch x sequence length).  Streaming, one pass.
+ *   packed row t = DENSE pack of q[t][j] = quant(kv[t][R[j]], cluster(j))
+ * kv       device fp16 [T][C], natural channel order (channel = head*head_dim + d).
+ * R        device int32 [C] or NULL (identity: the cache is already in R order).
+ * bounds, s, z host; bits in {3, 4, 8}.
+ * packed   device uint8 [T][C*bits/8].
+ * Limits: C % 8 == 0, C <= RPTQ_MAX_K, and C % 32 == 0 when bits == 3.
+ */
+int rptq_kv_quant_pack(const uint16_t* kv, int64_t T, int32_t C, const int32_t* R,
+                       const int32_t* bounds, int32_t g, const float* s, const int32_t* z,
+                       int32_t bits, uint8_t* packed, void* stream);
+
+/*
+ * K/V-cache dequantize, back to natural channel order (quantization lecture
+ * 1.3: W = S (Wq - Z)):
+ *   out[t][R[j]] = fp16_rne( fp32( s_c * (q[t][j] - z_c) ) )
+ * packed   device uint8 [T][C*bits/8] (DENSE, from rptq_kv_quant_pack).
+ * out      device fp16 [T][C].  Other arguments and limits as rptq_kv_quant_pack.
+ */
+int rptq_kv_dequant(const uint8_t* packed, int64_t T, int32_t C, const int32_t* R,
+                    const int32_t* bounds, int32_t g, const float* s, const int32_t* z,
+                    int32_t bits, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------- calibration
+ * Offline steps that produce R, bounds, s, z (RPTQ write-up, method section:
+ * run calibration data, record each channel's max and min, KMeans on the
+ * (max, min) points into g clusters, reorder, per-cluster parameters).
+ */
+
+/*
+ * Per-channel max and min over M calibration rows, in NATURAL channel order.
+ *   mode RPTQ_IN_FP16_RAW (0): statistics of LayerNorm(x; gamma, beta, eps)
+ *        (gamma, beta device fp32 [K], natural order), computed like the
+ *        fused kernel computes it;
+ *   mode 2 (raw): statistics of x itself (K/V cache); gamma, beta ignored.
+ * x device fp16 [M][K]; mx, mn device fp32 [K] (overwritten).
+ * Limits: K % 8 == 0, K <= RPTQ_MAX_K, M >= 1.
+ */
+#define RPTQ_CALIB_RAW 2
+int rptq_calib_minmax(const uint16_t* x, int32_t mode, int64_t M, int32_t K,
+                      const float* gamma, const float* beta, float eps,
+                      float* mx, float* mn, void* stream);
+
+/*
+ * KMeans over the points (mx[k], mn[k]) and the reorder index (host only).
+ * Seeding is k-means++ driven by the caller's uniforms init_u (host double
+ * [n_init * g], each in [0, 1)): the first centre is point floor(u * K), the
+ * next ones are drawn with probability proportional to the squared distance
+ * to the nearest chosen centre.  Lloyd iterations (nearest centre, ties to the
+ * lowest index; centre = mean; an empty cluster is re-seeded at the point
+ * farthest from its centre) stop when no label changes or after max_iter.
+ * The run with the lowest inertia wins (ties: earliest).  Clusters are then
+ * ordered by centroid min, then centroid max, then lowest channel; channels
+ * inside a cluster keep ascending order.
+ * mx, mn host fp32 [K]; R host int32 [K]; bounds host int32 [g+1].
+ */
+int rptq_kmeans_reorder(const float* mx, const float* mn, int32_t K, int32_t g,
+                        const double* init_u, int32_t n_init, int32_t max_iter,
+                        int32_t* R, int32_t* bounds);
+
+/*
+ * Per-cluster (s, z) from the channel ranges (host only).  lo = min of the
+ * cluster's channel minima, hi = max of its maxima (fp32 inputs, fp64 math):
+ *   s = fp32((hi - lo) / qmax), at least max(|lo|, |hi|) * 2^-21, 1 if zero
+ *   z = rne(-lo / s)
+ * mx, mn host fp32 [K] natural order; R host int32 [K] or NULL; bounds host.
+ */
+int rptq_cluster_params(const float* mx, const float* mn, const int32_t* R,
+                        const int32_t* bounds, int32_t g, int32_t bits,
+                        float* s, int32_t* z);
+
+/*
+ * Symmetric per-output-channel round-to-nearest weight quantization (host):
+ *   s_w[n] = max_k |W[k][n]| / (2^(wb-1) - 1)   (1 for an all-zero column)
+ *   wq[k][n] = clip(rne(W[k][n] / s_w[n]), -(2^(wb-1)-1), 2^(wb-1)-1)
+ * W host fp32 [K][N]; wq host int8 [K][N]; s_w host fp32 [N]; w_bits in {4, 8}.
+ */
+int rptq_quantize_weights(const float* W, int32_t K, int32_t N, int32_t w_bits,
+                          int8_t* wq, float* s_w);
+
+/*
+ * Reorder, pad and pack quantized weights for rptq_qgemm (host):
+ *   W'[j][n] = wq[R[j]][n];  w_packed row n = the SEG32-padded sequence
+ *   W'[.][n] (pad entries 0) in w_bits-bit two's complement, grouped like the
+ *   activation codes; colsum[c][n] = sum_{j in c} W'[j][n].
+ * wq host int8 [K][N] natural rows, values in [-(2^(wb-1)-1), 2^(wb-1)-1];
+ * R host int32 [K] or NULL; bounds host;
+ * w_packed host uint8 [N][rptq_weights_row_bytes(bounds, g, w_bits)];
+ * colsum host int32 [g][N].
+ */
+int rptq_pack_weights(const int8_t* wq, int32_t K, int32_t N, int32_t w_bits,
+                      const int32_t* R, const int32_t* bounds, int32_t g,
+                      uint8_t* w_packed, int32_t* colsum);
+
+/* ---------------------------------------------------------- sizes, errors */
+
+/* K_pad of the SEG32 layout; -1 on invalid bounds. */
+int32_t rptq_codes_kpad(const int32_t* bounds, int32_t g);
+/* SEG32 row stride in bytes for activation codes; -1 on invalid input. */
+int64_t rptq_codes_row_bytes(const int32_t* bounds, int32_t g, int32_t bits);
+/* Row stride of w_packed in bytes (K_pad * w_bits / 8); -1 on invalid input. */
+int64_t rptq_weights_row_bytes(const int32_t* bounds, int32_t g, int32_t w_bits);
+/* DENSE K/V row stride in bytes (C * bits / 8); -1 on invalid input. */
+int64_t rptq_kv_row_bytes(int32_t C, int32_t bits);
+
+const char* rptq_status_string(int status);
+/* Message describing the calling thread's most recent failure ("" if none). */
+const char* rptq_last_error(void);
+/* Library version string. */
+const char* rptq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RPTQ_H */

@@ -1,0 +1,266 @@
+"""MI355X (gfx950) RPTQ hot path: thin Python binding of the C ABI in
+``include/rptq.h`` (library ``librptq.so`` built in-tree by ``build.py``).
+
+Each ``rptq_*`` function here has the name of the C entry point it wraps and
+only marshals arguments: torch tensors supply device memory and the current
+HIP stream, small host arrays (bounds, s, z) are passed as numpy arrays.
+Every step of the hot path runs in the library's HIP kernels; there is no
+fallback -- if the library is missing or fails, the call raises.
+
+``import torch`` happens before the library is loaded so that the library's
+HIP runtime dependency binds to the runtime torch has already loaded.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch  # noqa: F401  (must precede loading librptq.so)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librptq.so")
+
+RPTQ_OK = 0
+RPTQ_ERR_INVALID_ARG = -1
+RPTQ_ERR_UNSUPPORTED = -2
+RPTQ_ERR_ALIGNMENT = -3
+RPTQ_ERR_HIP = -4
+RPTQ_IN_FP16_RAW = 0
+RPTQ_IN_FP32_NORMALIZED = 1
+RPTQ_CALIB_RAW = 2
+RPTQ_MAX_CLUSTERS = 64
+RPTQ_MAX_K = 16384
+
+EXPORTED = [
+    "rptq_ln_reorder_quant", "rptq_qgemm", "rptq_kv_quant_pack", "rptq_kv_dequant",
+    "rptq_calib_minmax", "rptq_kmeans_reorder", "rptq_cluster_params", "rptq_quantize_weights",
+    "rptq_pack_weights", "rptq_codes_kpad", "rptq_codes_row_bytes", "rptq_weights_row_bytes",
+    "rptq_kv_row_bytes", "rptq_status_string", "rptq_last_error", "rptq_version",
+]
+
+
+class RptqError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where} failed: status {status} ({_status_name(status)}): {detail}")
+        self.status = status
+
+
+def _status_name(st: int) -> str:
+    return {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "misaligned pointer",
+            -4: "HIP error"}.get(st, "unknown")
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+
+def lib() -> ctypes.CDLL:
+    """Load librptq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python post_quantization_layernorm_amd/build.py` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "rptq_ln_reorder_quant": (_I32, [_P, _I32, _I64, _I32, _P, _P, ctypes.c_float, _P, _P, _I32,
+                                             _P, _P, _I32, _P, _P]),
+            "rptq_qgemm": (_I32, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
+            "rptq_kv_quant_pack": (_I32, [_P, _I64, _I32, _P, _P, _I32, _P, _P, _I32, _P, _P]),
+            "rptq_kv_dequant": (_I32, [_P, _I64, _I32, _P, _P, _I32, _P, _P, _I32, _P, _P]),
+            "rptq_calib_minmax": (_I32, [_P, _I32, _I64, _I32, _P, _P, ctypes.c_float, _P, _P, _P]),
+            "rptq_kmeans_reorder": (_I32, [_P, _P, _I32, _I32, _P, _I32, _I32, _P, _P]),
+            "rptq_cluster_params": (_I32, [_P, _P, _P, _P, _I32, _I32, _P, _P]),
+            "rptq_quantize_weights": (_I32, [_P, _I32, _I32, _I32, _P, _P]),
+            "rptq_pack_weights": (_I32, [_P, _I32, _I32, _I32, _P, _P, _I32, _P, _P]),
+            "rptq_codes_kpad": (_I32, [_P, _I32]),
+            "rptq_codes_row_bytes": (_I64, [_P, _I32, _I32]),
+            "rptq_weights_row_bytes": (_I64, [_P, _I32, _I32]),
+            "rptq_kv_row_bytes": (_I64, [_I32, _I32]),
+            "rptq_status_string": (ctypes.c_char_p, [_I32]),
+            "rptq_last_error": (ctypes.c_char_p, []),
+            "rptq_version": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(st: int, where: str):
+    if st != RPTQ_OK:
+        raise RptqError(st, where, lib().rptq_last_error().decode())
+
+
+def _h(a, dtype):
+    """Host numpy array of the given dtype, contiguous."""
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _hp(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dp(t):
+    """Device pointer of a tensor (or None)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("expected a torch tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("device tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------------------- sizes
+def rptq_codes_kpad(bounds) -> int:
+    b = _h(bounds, np.int32)
+    return int(lib().rptq_codes_kpad(_hp(b), b.size - 1))
+
+
+def rptq_codes_row_bytes(bounds, bits: int) -> int:
+    b = _h(bounds, np.int32)
+    return int(lib().rptq_codes_row_bytes(_hp(b), b.size - 1, bits))
+
+
+def rptq_weights_row_bytes(bounds, w_bits: int) -> int:
+    b = _h(bounds, np.int32)
+    return int(lib().rptq_weights_row_bytes(_hp(b), b.size - 1, w_bits))
+
+
+def rptq_kv_row_bytes(C: int, bits: int) -> int:
+    return int(lib().rptq_kv_row_bytes(C, bits))
+
+
+def rptq_version() -> str:
+    return lib().rptq_version().decode()
+
+
+# ---------------------------------------------------------------------------- hot path
+def rptq_ln_reorder_quant(x, R, gamma_r, beta_r, bounds, s, z, bits, eps=1e-5,
+                          in_mode=RPTQ_IN_FP16_RAW, out=None, stream=None):
+    """x: cuda fp16 [M][K] (mode 0) or fp32 [M][K] R-ordered (mode 1).
+    Returns cuda uint8 [M][row_bytes] SEG32 codes."""
+    M, K = x.shape
+    b = _h(bounds, np.int32); sh = _h(s, np.float32); zh = _h(z, np.int32)
+    rb = rptq_codes_row_bytes(b, bits)
+    if rb < 0:
+        _check(RPTQ_ERR_INVALID_ARG, "rptq_codes_row_bytes")
+    if out is None:
+        out = torch.empty((M, rb), dtype=torch.uint8, device=x.device)
+    st = lib().rptq_ln_reorder_quant(_dp(x), in_mode, M, K, _dp(gamma_r), _dp(beta_r), eps, _dp(R),
+                                     _hp(b), b.size - 1, _hp(sh), _hp(zh), bits, _dp(out), _stream(stream))
+    _check(st, "rptq_ln_reorder_quant")
+    return out
+
+
+def rptq_qgemm(codes, M, K, N, bounds, s, z, a_bits, w_packed, w_bits, s_w, colsum, out=None,
+               acc_debug=None, stream=None):
+    """codes: cuda uint8 SEG32 [M][row_bytes]; w_packed: cuda uint8 [N][K_pad*w_bits/8];
+    s_w: cuda fp32 [N]; colsum: cuda int32 [g][N].  Returns Y cuda fp32 [M][N]."""
+    b = _h(bounds, np.int32); sh = _h(s, np.float32); zh = _h(z, np.int32)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    st = lib().rptq_qgemm(_dp(codes), M, K, N, _hp(b), b.size - 1, _hp(sh), _hp(zh), a_bits, _dp(w_packed),
+                          w_bits, _dp(s_w), _dp(colsum), _dp(out), _dp(acc_debug), _stream(stream))
+    _check(st, "rptq_qgemm")
+    return out
+
+
+def rptq_kv_quant_pack(kv, R, bounds, s, z, bits, out=None, stream=None):
+    """kv: cuda fp16 [T][C] natural order.  Returns cuda uint8 [T][C*bits/8]."""
+    T, C = kv.shape
+    b = _h(bounds, np.int32); sh = _h(s, np.float32); zh = _h(z, np.int32)
+    if out is None:
+        rb = rptq_kv_row_bytes(C, bits)
+        if rb < 0:
+            _check(RPTQ_ERR_UNSUPPORTED, "rptq_kv_row_bytes")
+        out = torch.empty((T, rb), dtype=torch.uint8, device=kv.device)
+    st = lib().rptq_kv_quant_pack(_dp(kv), T, C, _dp(R), _hp(b), b.size - 1, _hp(sh), _hp(zh), bits,
+                                  _dp(out), _stream(stream))
+    _check(st, "rptq_kv_quant_pack")
+    return out
+
+
+def rptq_kv_dequant(packed, C, R, bounds, s, z, bits, out=None, stream=None):
+    """packed: cuda uint8 [T][C*bits/8].  Returns cuda fp16 [T][C] natural order."""
+    T = packed.shape[0]
+    b = _h(bounds, np.int32); sh = _h(s, np.float32); zh = _h(z, np.int32)
+    if out is None:
+        out = torch.empty((T, C), dtype=torch.float16, device=packed.device)
+    st = lib().rptq_kv_dequant(_dp(packed), T, C, _dp(R), _hp(b), b.size - 1, _hp(sh), _hp(zh), bits,
+                               _dp(out), _stream(stream))
+    _check(st, "rptq_kv_dequant")
+    return out
+
+
+# ---------------------------------------------------------------------------- calibration
+def rptq_calib_minmax(x, mode=RPTQ_IN_FP16_RAW, gamma=None, beta=None, eps=1e-5, stream=None):
+    """x: cuda fp16 [M][K].  Returns (mx, mn) cuda fp32 [K], natural order."""
+    M, K = x.shape
+    mx = torch.empty(K, dtype=torch.float32, device=x.device)
+    mn = torch.empty(K, dtype=torch.float32, device=x.device)
+    st = lib().rptq_calib_minmax(_dp(x), mode, M, K, _dp(gamma), _dp(beta), eps, _dp(mx), _dp(mn),
+                                 _stream(stream))
+    _check(st, "rptq_calib_minmax")
+    return mx, mn
+
+
+def rptq_kmeans_reorder(mx, mn, g, init_u, n_init=10, max_iter=300):
+    """Host.  Returns (R int32 [K], bounds int32 [g+1])."""
+    mxh = _h(mx, np.float32); mnh = _h(mn, np.float32); u = _h(init_u, np.float64)
+    K = mxh.size
+    if u.size < n_init * g:
+        raise ValueError("init_u needs n_init * g uniforms")
+    R = np.empty(K, np.int32); bounds = np.empty(g + 1, np.int32)
+    _check(lib().rptq_kmeans_reorder(_hp(mxh), _hp(mnh), K, g, _hp(u), n_init, max_iter, _hp(R), _hp(bounds)),
+           "rptq_kmeans_reorder")
+    return R, bounds
+
+
+def rptq_cluster_params(mx, mn, R, bounds, bits):
+    """Host.  Returns (s fp32 [g], z int32 [g])."""
+    mxh = _h(mx, np.float32); mnh = _h(mn, np.float32)
+    Rh = None if R is None else _h(R, np.int32)
+    b = _h(bounds, np.int32); g = b.size - 1
+    s = np.empty(g, np.float32); z = np.empty(g, np.int32)
+    _check(lib().rptq_cluster_params(_hp(mxh), _hp(mnh), _hp(Rh), _hp(b), g, bits, _hp(s), _hp(z)),
+           "rptq_cluster_params")
+    return s, z
+
+
+def rptq_quantize_weights(W, w_bits):
+    """Host.  W fp32 [K][N] -> (wq int8 [K][N], s_w fp32 [N])."""
+    Wh = _h(W, np.float32)
+    K, N = Wh.shape
+    wq = np.empty((K, N), np.int8); sw = np.empty(N, np.float32)
+    _check(lib().rptq_quantize_weights(_hp(Wh), K, N, w_bits, _hp(wq), _hp(sw)), "rptq_quantize_weights")
+    return wq, sw
+
+
+def rptq_pack_weights(wq, R, bounds, w_bits):
+    """Host.  Returns (w_packed uint8 [N][K_pad*w_bits/8], colsum int32 [g][N])."""
+    wqh = _h(wq, np.int8)
+    K, N = wqh.shape
+    Rh = None if R is None else _h(R, np.int32)
+    b = _h(bounds, np.int32); g = b.size - 1
+    rb = rptq_weights_row_bytes(b, w_bits)
+    if rb < 0:
+        _check(RPTQ_ERR_INVALID_ARG, "rptq_weights_row_bytes")
+    wp = np.empty((N, rb), np.uint8); cs = np.empty((g, N), np.int32)
+    _check(lib().rptq_pack_weights(_hp(wqh), K, N, w_bits, _hp(Rh), _hp(b), g, _hp(wp), _hp(cs)),
+           "rptq_pack_weights")
+    return wp, cs

@@ -1,0 +1,138 @@
+// Device-side helpers shared by the library's HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <cstdint>
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include "rptq_internal.h"
+
+namespace rptq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Code of one value v with a cluster's fp32 reciprocal scale inv_s and
+// zb = z - kRoundMagicBits:
+//   u = fl(v * inv_s + 1.5*2^23)    one rounding of the exact product: for
+//                                   |v*inv_s| <= 2^22 this is 1.5*2^23 +
+//                                   rne(v*inv_s), held in the low mantissa bits
+//   clamp u to [2^23, 2^24]         |v*inv_s| >= 2^22 saturates (|z| <= 2^21
+//                                   makes the final clip decide those anyway)
+//   q = clip(bits(u) - bits(1.5*2^23) + z, 0, qmax)
+__device__ __forceinline__ int quant_code(float v, float inv_s, int zb, int qmax) {
+    float u = __builtin_fmaf(v, inv_s, kRoundMagic);
+    u = __builtin_amdgcn_fmed3f(u, 8388608.0f, 16777216.0f);
+    const int k = __builtin_bit_cast(int, u) + zb;
+    return __builtin_elementwise_max(__builtin_elementwise_min(k, qmax), 0);
+}
+
+// Wave64 sum.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Sum over a 256-thread workgroup; `scratch` holds 4 floats.  Ends with a
+// barrier, so `scratch` may be reused right after.
+__device__ __forceinline__ float block_sum_256(float v, float* scratch) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) scratch[w] = v;
+    __syncthreads();
+    const float t = scratch[0] + scratch[1] + scratch[2] + scratch[3];
+    __syncthreads();
+    return t;
+}
+
+// Positions of the 8 codes a "unit" covers, in a row laid out in groups (see
+// rptq.h).  For 4- and 8-bit rows a unit is 8 consecutive codes; for 3-bit
+// rows a unit is byte lane `bl` of a 32-code group: codes bl, bl+4, ..., bl+28.
+template <int BITS>
+struct UnitGeom {
+    __device__ __forceinline__ static int first(int unit) {
+        return BITS == 3 ? 32 * (unit >> 2) + (unit & 3) : 8 * unit;
+    }
+    static constexpr int stride = BITS == 3 ? 4 : 1;
+    // byte offset of the unit's first output byte in the packed row
+    __device__ __forceinline__ static int out_byte(int unit) {
+        return BITS == 3 ? 12 * (unit >> 2) + (unit & 3) : unit * BITS;
+    }
+};
+
+// Pack the 8 codes of a unit (q[e] is the code at position first + e*stride)
+// and store them into the packed row `out` (LDS) at the unit's byte offset.
+template <int BITS>
+__device__ __forceinline__ void store_unit(unsigned char* out, int unit, const int (&q)[8]) {
+    const int ob = UnitGeom<BITS>::out_byte(unit);
+    if constexpr (BITS == 8) {
+        uint2 v;
+        v.x = (uint32_t)q[0] | (uint32_t)q[1] << 8 | (uint32_t)q[2] << 16 | (uint32_t)q[3] << 24;
+        v.y = (uint32_t)q[4] | (uint32_t)q[5] << 8 | (uint32_t)q[6] << 16 | (uint32_t)q[7] << 24;
+        *reinterpret_cast<uint2*>(out + ob) = v;
+    } else if constexpr (BITS == 4) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v |= ((uint32_t)q[i] | (uint32_t)q[4 + i] << 4) << (8 * i);
+        *reinterpret_cast<uint32_t*>(out + ob) = v;
+    } else {
+        // byte lane bl of words d0, d1, d2 of the group
+        out[ob] = (unsigned char)(q[0] | q[1] << 3 | (q[6] & 3) << 6);
+        out[ob + 4] = (unsigned char)(q[2] | q[3] << 3 | (q[7] & 3) << 6);
+        out[ob + 8] = (unsigned char)(q[4] | q[5] << 3 | (q[6] >> 2) << 6 | (q[7] >> 2) << 7);
+    }
+}
+
+// Inverse of store_unit: the 8 codes of a unit from a packed row (LDS).
+template <int BITS>
+__device__ __forceinline__ void load_unit(const unsigned char* in, int unit, int (&q)[8]) {
+    const int ob = UnitGeom<BITS>::out_byte(unit);
+    if constexpr (BITS == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(in + ob);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { q[i] = (v.x >> (8 * i)) & 255; q[4 + i] = (v.y >> (8 * i)) & 255; }
+    } else if constexpr (BITS == 4) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(in + ob);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { q[i] = (v >> (8 * i)) & 15; q[4 + i] = (v >> (8 * i + 4)) & 15; }
+    } else {
+        const int b0 = in[ob], b1 = in[ob + 4], b2 = in[ob + 8];
+        q[0] = b0 & 7; q[1] = (b0 >> 3) & 7;
+        q[2] = b1 & 7; q[3] = (b1 >> 3) & 7;
+        q[4] = b2 & 7; q[5] = (b2 >> 3) & 7;
+        q[6] = (b0 >> 6) | ((b2 >> 6) & 1) << 2;
+        q[7] = (b1 >> 6) | ((b2 >> 7) & 1) << 2;
+    }
+}
+
+// Cluster holding reordered (unpadded) position j.
+__device__ __forceinline__ int cluster_of_pos(const ClusterArgs& ca, int j) {
+    int c = 0;
+    while (c + 1 < ca.g && j >= ca.bounds[c + 1]) ++c;
+    return c;
+}
+
+// Cluster holding SEG32 padded position p.
+__device__ __forceinline__ int cluster_of_padded(const ClusterArgs& ca, int p) {
+    int c = 0;
+    while (c + 1 < ca.g && p >= ca.off[c + 1]) ++c;
+    return c;
+}
+
+// Copy `bytes` (a multiple of 4) from LDS to global memory with the whole
+// workgroup; 16-byte stores when both ends allow it.
+__device__ __forceinline__ void store_row(uint8_t* __restrict__ dst, const unsigned char* src,
+                                          int64_t bytes) {
+    if ((bytes & 15) == 0 && ((uintptr_t)dst & 15) == 0) {
+        const int n = (int)(bytes >> 4);
+        for (int i = threadIdx.x; i < n; i += blockDim.x)
+            reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
+    } else {
+        const int n = (int)(bytes >> 2);
+        for (int i = threadIdx.x; i < n; i += blockDim.x)
+            reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(src)[i];
+    }
+}
+
+}  // namespace rptq

@@ -1,0 +1,68 @@
+// Internal declarations shared by the host-side C ABI (rptq_api.cpp) and the
+// HIP kernel sources of the library.  Not installed; not part of the ABI.
+#pragma once
+
+#include <cstdint>
+#include <hip/hip_runtime.h>
+
+namespace rptq {
+
+constexpr int kMaxClusters = 64;
+constexpr int kMaxK = 16384;
+constexpr int kBlock = 256;            // threads per workgroup of the streaming kernels
+
+// Cluster table, passed by value as a kernel argument (about 1.6 KB, well
+// under the kernel-argument limit).  Built and validated on the host.
+struct ClusterArgs {
+    int32_t g;
+    int32_t K;                          // real channels (bounds[g])
+    int32_t K_pad;                      // SEG32 padded length (0 when unused)
+    int32_t bits;
+    int32_t bounds[kMaxClusters + 1];   // reordered-position boundaries
+    int32_t off[kMaxClusters + 1];      // SEG32 padded offsets
+    float inv_s[kMaxClusters];          // fp32(1 / s_c)
+    float s[kMaxClusters];
+    int32_t z[kMaxClusters];
+};
+
+// Magic constant 1.5 * 2^23: adding it to |v| < 2^22 rounds v half-to-even to
+// an integer held in the low mantissa bits.
+constexpr float kRoundMagic = 12582912.0f;
+constexpr int32_t kRoundMagicBits = 0x4B400000;
+
+// Per-cluster tables of the GEMM, passed by value.
+struct GemmArgs {
+    int32_t g;
+    int32_t nsteps;                        // K_pad / 32
+    int32_t step_end[kMaxClusters];        // exclusive end (in 32-code steps) of cluster c
+    float scale[kMaxClusters];             // s_c divided by the weight pre-scale
+    double sz[kMaxClusters];               // s_c * (z_c - code offset), for the epilogue
+    int32_t code_offset;                   // 128 for 8-bit activations (stored q - 128), else 0
+};
+
+// Launchers (one per kernel family); each returns the launch status.
+hipError_t launch_ln_reorder_quant(const void* x, int in_mode, int64_t M, int32_t K,
+                                   const float* gamma_r, const float* beta_r, float eps,
+                                   const int32_t* R, const ClusterArgs& ca, int64_t row_bytes,
+                                   uint8_t* codes, hipStream_t stream);
+
+hipError_t launch_kv_quant_pack(const uint16_t* kv, int64_t T, int32_t C, const int32_t* R,
+                                const ClusterArgs& ca, uint8_t* packed, hipStream_t stream);
+
+hipError_t launch_kv_dequant(const uint8_t* packed, int64_t T, int32_t C, const int32_t* R,
+                             const ClusterArgs& ca, uint16_t* out, hipStream_t stream);
+
+hipError_t launch_calib_minmax(const uint16_t* x, int mode, int64_t M, int32_t K,
+                               const float* gamma, const float* beta, float eps,
+                               float* mx, float* mn, hipStream_t stream);
+
+hipError_t launch_qgemm(const uint8_t* codes, int64_t M, int32_t N, int64_t a_row_bytes,
+                        int a_bits, const uint8_t* w_packed, int64_t w_row_bytes, int w_bits,
+                        const GemmArgs& ga, const float* s_w, const int32_t* colsum,
+                        float* Y, int32_t* acc_debug, hipStream_t stream);
+
+// Number of workgroups a persistent streaming kernel should launch: the
+// device's compute units times the resident workgroups per unit.
+int persistent_grid(const void* kernel, int block, size_t lds_bytes, int64_t rows);
+
+}  // namespace rptq

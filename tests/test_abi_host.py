@@ -1,0 +1,219 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, rejects bad arguments on the host before any HIP call, and
+its host-side calibration / weight helpers agree with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synthetic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def P():
+    import post_quantization_layernorm_amd as P
+    P.lib()
+    return P
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "rptq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rptq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(P):
+    names = _header_functions()
+    assert len(names) >= 16
+    lib = ctypes.CDLL(P.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(P.EXPORTED)
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import post_quantization_layernorm_amd as P
+    monkeypatch.setattr(P, "_lib", None)
+    monkeypatch.setattr(P, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        P.lib()
+
+
+def _vp(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced on error paths
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def _ln(P, **kw):
+    a = dict(x=FAKE, mode=0, M=4, K=64, gamma=FAKE, beta=FAKE, eps=1e-5, R=None,
+             bounds=np.array([0, 16, 64], np.int32), s=np.array([0.1, 0.2], np.float32),
+             z=np.array([3, -2], np.int32), bits=4, codes=FAKE)
+    a.update(kw)
+    g = kw.get("g", a["bounds"].size - 1)
+    return P.lib().rptq_ln_reorder_quant(a["x"], a["mode"], a["M"], a["K"], a["gamma"], a["beta"], a["eps"],
+                                         a["R"], _vp(a["bounds"]), g, _vp(a["s"]), _vp(a["z"]),
+                                         a["bits"], a["codes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=5), -1), (dict(bits=2), -1), (dict(mode=7), -1), (dict(M=-1), -1), (dict(K=0), -1),
+    (dict(bounds=np.array([1, 16, 64], np.int32)), -1),
+    (dict(bounds=np.array([0, 16, 60], np.int32)), -1),
+    (dict(bounds=np.array([0, 16, 16, 64], np.int32), s=np.ones(3, np.float32), z=np.zeros(3, np.int32)), -1),
+    (dict(bounds=np.array([0, 64], np.int32), g=0), -1),
+    (dict(bounds=np.arange(66, dtype=np.int32), K=65, g=65), -1),
+    (dict(s=np.array([0.0, 0.2], np.float32)), -1), (dict(s=np.array([np.nan, 0.2], np.float32)), -1),
+    (dict(s=np.array([-1.0, 0.2], np.float32)), -1), (dict(s=np.array([np.inf, 0.2], np.float32)), -1),
+    (dict(s=np.array([1e-45, 0.2], np.float32)), -1),
+    (dict(z=np.array([2 ** 21 + 1, 0], np.int32)), -1), (dict(z=np.array([0, -(2 ** 21) - 1], np.int32)), -1),
+    (dict(eps=0.0), -1), (dict(eps=-1.0), -1), (dict(eps=float("nan")), -1),
+    (dict(gamma=None), -1), (dict(x=None), -1), (dict(codes=None), -1),
+    (dict(K=60, bounds=np.array([0, 16, 60], np.int32)), -2),
+    (dict(K=16392, bounds=np.array([0, 16, 16392], np.int32)), -2),
+    (dict(x=MISALIGNED), -3), (dict(codes=MISALIGNED), -3), (dict(R=MISALIGNED), -3),
+])
+def test_ln_reorder_quant_rejects(P, kw, status):
+    assert _ln(P, **kw) == status
+    assert P.lib().rptq_last_error().decode()
+
+
+def test_ln_reorder_quant_m0_is_noop(P):
+    assert _ln(P, M=0, x=None, codes=None) == 0
+    # quant-only mode ignores gamma / beta / eps
+    assert _ln(P, M=0, mode=1, gamma=None, beta=None, eps=0.0) == 0
+
+
+def _gemm(P, **kw):
+    a = dict(codes=FAKE, M=8, K=64, N=32, bounds=np.array([0, 16, 64], np.int32),
+             s=np.array([0.1, 0.2], np.float32), z=np.array([3, -2], np.int32), a_bits=4, w=FAKE, w_bits=4,
+             s_w=FAKE, colsum=FAKE, Y=FAKE, acc=None)
+    a.update(kw)
+    return P.lib().rptq_qgemm(a["codes"], a["M"], a["K"], a["N"], _vp(a["bounds"]), a["bounds"].size - 1,
+                              _vp(a["s"]), _vp(a["z"]), a["a_bits"], a["w"], a["w_bits"], a["s_w"], a["colsum"],
+                              a["Y"], a["acc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a_bits=2), -1), (dict(w_bits=3), -1), (dict(w_bits=16), -1), (dict(N=0), -1), (dict(M=-3), -1),
+    (dict(K=63), -1), (dict(s=np.array([0.1, -0.2], np.float32)), -1), (dict(w=None), -1),
+    (dict(colsum=None), -1), (dict(Y=None), -1), (dict(s_w=None), -1),
+    (dict(K=16392, bounds=np.array([0, 8, 16392], np.int32)), -2),
+    (dict(codes=MISALIGNED), -3), (dict(Y=MISALIGNED), -3), (dict(acc=MISALIGNED), -3),
+])
+def test_qgemm_rejects(P, kw, status):
+    assert _gemm(P, **kw) == status
+
+
+def test_qgemm_m0_is_noop(P):
+    assert _gemm(P, M=0, codes=None, Y=None) == 0
+
+
+def _kv(P, fn, **kw):
+    a = dict(src=FAKE, T=10, C=64, R=None, bounds=np.array([0, 32, 64], np.int32),
+             s=np.array([0.1, 0.2], np.float32), z=np.array([3, -2], np.int32), bits=3, dst=FAKE)
+    a.update(kw)
+    f = getattr(P.lib(), fn)
+    return f(a["src"], a["T"], a["C"], a["R"], _vp(a["bounds"]), a["bounds"].size - 1, _vp(a["s"]),
+             _vp(a["z"]), a["bits"], a["dst"], None)
+
+
+@pytest.mark.parametrize("fn", ["rptq_kv_quant_pack", "rptq_kv_dequant"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=1), -1), (dict(T=-1), -1), (dict(C=0), -1), (dict(src=None), -1), (dict(dst=None), -1),
+    (dict(z=np.array([0, 1 << 22], np.int32)), -1),
+    (dict(C=72, bounds=np.array([0, 32, 72], np.int32)), -2),                 # 3-bit needs C % 32
+    (dict(C=60, bits=4, bounds=np.array([0, 32, 60], np.int32)), -2),         # C % 8
+    (dict(src=MISALIGNED), -3), (dict(R=MISALIGNED), -3),
+])
+def test_kv_rejects(P, fn, kw, status):
+    assert _kv(P, fn, **kw) == status
+
+
+@pytest.mark.parametrize("fn", ["rptq_kv_quant_pack", "rptq_kv_dequant"])
+def test_kv_t0_is_noop(P, fn):
+    assert _kv(P, fn, T=0, src=None, dst=None) == 0
+    assert _kv(P, fn, T=0, C=72, bits=4, bounds=np.array([0, 32, 72], np.int32)) == 0
+
+
+def test_status_strings_and_sizes(P):
+    L = P.lib()
+    assert L.rptq_status_string(0) == b"ok" and L.rptq_status_string(-4) == b"HIP error"
+    b = np.array([0, 1, 32, 64, 97, 192], np.int32)
+    assert P.rptq_codes_kpad(b) == 256
+    assert P.rptq_codes_row_bytes(b, 3) == 96 and P.rptq_codes_row_bytes(b, 4) == 128
+    assert P.rptq_codes_row_bytes(b, 8) == 256 and P.rptq_weights_row_bytes(b, 4) == 128
+    assert P.rptq_codes_row_bytes(b, 5) == -1
+    assert P.rptq_kv_row_bytes(9216, 3) == 3456 and P.rptq_kv_row_bytes(72, 3) == -1
+
+
+# ----------------------------------------------------------------------------- host helpers vs oracle
+def test_host_kmeans_reorder_matches_oracle(P, orc):
+    for name, w in synthetic.WORKLOADS.items():
+        K = min(w.K, 1536)
+        mu, sg = synthetic.channel_params(K, w.seed, w.outlier_frac, range_ratio=w.range_ratio)
+        x = synthetic.tokens(256, mu, sg, w.seed, synthetic.STREAM_CALIB)
+        gamma, beta = synthetic.ln_params(K, w.seed)
+        mx, mn = orc.channel_minmax(orc.layernorm(x, gamma, beta))
+        u = synthetic.kmeans_uniforms(w.seed, 4, w.g)
+        R_o, b_o, s_o, z_o = orc.calibrate(mx, mn, w.g, w.a_bits, u, n_init=4)
+        R_p, b_p = P.rptq_kmeans_reorder(mx, mn, w.g, u, n_init=4)
+        assert np.array_equal(R_p, R_o), name
+        assert np.array_equal(b_p, b_o), name
+        s_p, z_p = P.rptq_cluster_params(mx, mn, R_p, b_p, w.a_bits)
+        assert np.array_equal(s_p, s_o) and np.array_equal(z_p, z_o), name
+
+
+def test_host_weight_quantization_matches_oracle(P, orc):
+    W = synthetic.weights(96, 40, 5)
+    W[:, 3] = 0
+    for wb in (4, 8):
+        wq_o, sw_o = orc.quantize_weights(W, wb)
+        wq_p, sw_p = P.rptq_quantize_weights(W, wb)
+        assert np.array_equal(wq_o, wq_p) and np.array_equal(sw_o, sw_p)
+
+
+@pytest.mark.parametrize("wb", [4, 8])
+def test_host_pack_weights_reorders_pads_and_sums(P, orc, wb):
+    r = np.random.default_rng(wb)
+    K, N = 100, 24
+    qm = 2 ** (wb - 1) - 1
+    wq = r.integers(-qm, qm + 1, (K, N)).astype(np.int8)
+    R = r.permutation(K).astype(np.int32)
+    bounds = np.array([0, 1, 33, 64, 100], np.int32)
+    wp, cs = P.rptq_pack_weights(wq, R, bounds, wb)
+    kp = orc.seg32_kpad(bounds)
+    assert wp.shape == (N, kp * wb // 8)
+    # the packed rows use the same group layout as activation codes (two's
+    # complement nibbles); decode with the oracle's unpacker
+    codes = orc.unpack_dense(wp, kp, wb).astype(np.int16)
+    if wb == 4:
+        codes = np.where(codes >= 8, codes - 16, codes)
+    else:
+        codes = np.where(codes >= 128, codes - 256, codes)
+    dense, pad = orc.unpack_seg32(orc.pack_dense(np.zeros((N, kp), np.uint8), 8), K, bounds, 8, return_pad=True)
+    # rebuild reordered weights from the padded sequence
+    off = 0
+    for c in range(bounds.size - 1):
+        n_c = bounds[c + 1] - bounds[c]
+        seg = codes[:, off:off + n_c]
+        assert np.array_equal(seg.T, wq[R[bounds[c]:bounds[c + 1]]].astype(np.int16))
+        assert not codes[:, off + n_c:off + (n_c + 31) // 32 * 32].any()
+        assert np.array_equal(cs[c], wq[R[bounds[c]:bounds[c + 1]]].astype(np.int64).sum(0))
+        off += (n_c + 31) // 32 * 32
+
+
+def test_host_helpers_reject(P):
+    with pytest.raises(P.RptqError):
+        P.rptq_pack_weights(np.full((8, 4), 9, np.int8), None, np.array([0, 8], np.int32), 4)   # |w| > 7
+    with pytest.raises(P.RptqError):
+        P.rptq_kmeans_reorder(np.zeros(4, np.float32), np.zeros(4, np.float32), 5, np.zeros(50))
+    with pytest.raises(P.RptqError):
+        P.rptq_cluster_params(np.zeros(4, np.float32), np.zeros(4, np.float32), None,
+                              np.array([0, 2, 2, 4], np.int32), 4)

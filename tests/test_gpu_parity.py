@@ -1,0 +1,240 @@
+"""GPU parity: every entry point of the C ABI against the oracle, element by
+element, on seeded inputs.  Bars: codes and int32 accumulators bit-exact;
+KV dequant fp16 bit-exact; fused LayerNorm codes within 0.1% of positions
+differing by at most 1; Y within 1e-3 relative L2."""
+import numpy as np
+import pytest
+
+import oracle as orc
+import synthetic
+from helpers import dev, explicit_case, layer_case, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def P():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import post_quantization_layernorm_amd as P
+    P.lib()
+    print(f"[gpu] {torch.cuda.get_device_name(0)} | {P.rptq_version()}", flush=True)
+    return P
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ----------------------------------------------------------------------------- K/V cache
+def _kv_params(kv, g, bits, seed, identity=False):
+    mx, mn = orc.channel_minmax(kv)
+    R, bounds, s, z = orc.calibrate(mx, mn, g, bits, synthetic.kmeans_uniforms(seed, 3, g), n_init=3)
+    if identity:
+        # the cache is already in reordered order: R = NULL on the device
+        kv = np.ascontiguousarray(kv[:, R])
+        R = None
+    return kv, R, bounds, s, z
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+@pytest.mark.parametrize("T,C,g,identity", [(333, 512, 8, False), (37, 9216, 32, False),
+                                             (5, 1024, 16, True), (1, 128, 4, False)])
+def test_kv_quant_pack_and_dequant_bit_exact(P, bits, T, C, g, identity):
+    _say("kv", bits, T, C, g, identity)
+    mu, sg = synthetic.channel_params(C, 40 + bits, 0.01)
+    kv = synthetic.tokens(T, mu, sg, 40 + bits, synthetic.STREAM_EVAL)
+    kvd, R, bounds, s, z = _kv_params(kv, g, bits, 40 + bits, identity)
+    want = orc.kv_quant_pack(kvd, R, bounds, s, z, bits)
+    Rd = None if R is None else dev(R)
+    got = P.rptq_kv_quant_pack(dev(kvd.view(np.int16)).view(torch.float16), Rd, bounds, s, z, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), want)
+    want_deq = orc.kv_dequant(want, C, R, bounds, s, z, bits)
+    got_deq = P.rptq_kv_dequant(dev(want), C, Rd, bounds, s, z, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(got_deq.cpu().numpy().view(np.uint16), want_deq)
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_kv_extremes_and_size_one_clusters(P, bits):
+    """inf / max-half inputs, clusters of one channel, zero points near +-2^21."""
+    C, T = 64, 9
+    r = np.random.default_rng(bits)
+    kv = (r.standard_normal((T, C)) * 50).astype(np.float16)
+    kv[0, :8] = [np.inf, -np.inf, 65504, -65504, 0.0, -0.0, 6e-8, -6e-8]
+    bounds = np.arange(C + 1, dtype=np.int32)                  # g = 64, one channel each
+    R = r.permutation(C).astype(np.int32)
+    s = r.uniform(1e-3, 10, C).astype(np.float32)
+    z = r.integers(-(2 ** 21), 2 ** 21 + 1, C).astype(np.int32)
+    z[:4] = [2 ** 21, -(2 ** 21), 0, (1 << bits) - 1]
+    want = orc.kv_quant_pack(kv, R, bounds, s, z, bits)
+    got = P.rptq_kv_quant_pack(dev(kv.view(np.int16)).view(torch.float16), dev(R), bounds, s, z, bits)
+    assert np.array_equal(got.cpu().numpy(), want)
+    want_deq = orc.kv_dequant(want, C, R, bounds, s, z, bits)
+    got_deq = P.rptq_kv_dequant(dev(want), C, dev(R), bounds, s, z, bits)
+    assert np.array_equal(got_deq.cpu().numpy().view(np.uint16), want_deq)
+
+
+# ----------------------------------------------------------------------------- LayerNorm + quant
+LN_SHAPES = [  # (M, K, g, outlier_frac, range_ratio)
+    (128, 768, 4, 0.01, None),          # OPT-125m-shaped
+    (70, 2048, 8, 0.005, None),         # OPT-1.3B-shaped
+    (33, 5120, 16, 0.0, 300.0),         # OPT-13B-shaped, 10x-300x channel ranges
+    (41, 9216, 32, 0.01, None),         # OPT-66B-shaped
+    (6, 16384, 64, 0.01, None),         # largest K, 512-thread path
+]
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+@pytest.mark.parametrize("shape", LN_SHAPES, ids=lambda s: f"K{s[1]}g{s[2]}")
+def test_ln_quant_only_mode_bit_exact(P, bits, shape):
+    M, K, g, frac, rr = shape
+    _say("ln quant-only", bits, shape)
+    c = layer_case(M, K, 8, g, bits, seed=K + bits, outlier_frac=frac, range_ratio=rr, with_weights=False)
+    y = orc.layernorm(c.x, c.gamma, c.beta, 1e-5, c.R)
+    y[0, : min(K, 16)] = [1e30, -1e30, np.inf, -np.inf, 0.0, -0.0, 3e-39, 1e-3] * (min(K, 16) // 8)
+    want = orc.pack_seg32(orc.quantize(y, c.bounds, c.s, c.z, bits), c.bounds, bits)
+    got = P.rptq_ln_reorder_quant(dev(y), None, None, None, c.bounds, c.s, c.z, bits,
+                                  in_mode=P.RPTQ_IN_FP32_NORMALIZED)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def _fused(P, c, bits, eps=1e-5):
+    gr, br = c.gamma[c.R], c.beta[c.R]
+    return P.rptq_ln_reorder_quant(dev(c.x.view(np.int16)).view(torch.float16), dev(c.R), dev(gr), dev(br),
+                                   c.bounds, c.s, c.z, bits, eps=eps)
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+@pytest.mark.parametrize("shape", LN_SHAPES, ids=lambda s: f"K{s[1]}g{s[2]}")
+def test_ln_fused_codes_within_tolerance(P, bits, shape):
+    M, K, g, frac, rr = shape
+    _say("ln fused", bits, shape)
+    c = layer_case(M, K, 8, g, bits, seed=K + bits, outlier_frac=frac, range_ratio=rr, with_weights=False)
+    want = orc.ln_reorder_quant(c.x, c.gamma, c.beta, 1e-5, c.R, c.bounds, c.s, c.z, bits)
+    got = _fused(P, c, bits).cpu().numpy()
+    qg, pad_g = orc.unpack_seg32(got, K, c.bounds, bits, return_pad=True)
+    qw = orc.unpack_seg32(want, K, c.bounds, bits)
+    assert not pad_g.any()
+    d = np.abs(qg.astype(np.int32) - qw.astype(np.int32))
+    assert d.max() <= 1
+    assert (d > 0).mean() <= 1e-3, (d > 0).mean()
+
+
+def test_ln_fused_edge_rows(P):
+    """M = 1, a constant row (zero variance), identity R, single cluster."""
+    K = 256
+    x = np.full((3, K), 7.0, np.float16)
+    x[1] = np.linspace(-100, 100, K).astype(np.float16)
+    x[2, ::2] = -3.0
+    gamma, beta = synthetic.ln_params(K, 3)
+    bounds = np.array([0, K], np.int32)
+    y = orc.layernorm(x, gamma, beta)
+    mx, mn = orc.channel_minmax(y)
+    s, z = orc.cluster_params(mx, mn, None, bounds, 4)
+    want = orc.ln_reorder_quant(x, gamma, beta, 1e-5, None, bounds, s, z, 4)
+    for M in (1, 3):
+        got = P.rptq_ln_reorder_quant(dev(x[:M].view(np.int16)).view(torch.float16), None, dev(gamma), dev(beta),
+                                      bounds, s, z, 4).cpu().numpy()
+        qg = orc.unpack_seg32(got, K, bounds, 4).astype(np.int32)
+        qw = orc.unpack_seg32(want[:M], K, bounds, 4).astype(np.int32)
+        assert np.abs(qg - qw).max() <= 1 and (qg != qw).mean() <= 1e-3
+
+
+def test_ln_m0_noop(P):
+    x = torch.empty((0, 64), dtype=torch.float16, device="cuda")
+    out = P.rptq_ln_reorder_quant(x, None, dev(np.ones(64, np.float32)), dev(np.zeros(64, np.float32)),
+                                  np.array([0, 64], np.int32), np.ones(1, np.float32), np.zeros(1, np.int32), 4)
+    assert out.shape[0] == 0
+
+
+# ----------------------------------------------------------------------------- GEMM
+def _gemm_inputs(P, c):
+    wp, cs = P.rptq_pack_weights(c.Wq, c.R, c.bounds, c.w_bits)
+    return dev(wp), dev(cs), dev(c.s_w)
+
+
+def _oracle_codes(c):
+    y = orc.layernorm(c.x, c.gamma, c.beta, 1e-5, c.R)
+    q = orc.quantize(y, c.bounds, c.s, c.z, c.a_bits)
+    return q, orc.pack_seg32(q, c.bounds, c.a_bits)
+
+
+GEMM_CASES = [  # (M, K, N, g, a_bits, w_bits)
+    (128, 768, 3072, 4, 8, 8),          # OPT-125m-shaped W8A8
+    (200, 2048, 392, 8, 4, 4),          # OPT-1.3B-shaped W4A4, ragged M and N
+    (96, 5120, 256, 16, 8, 4),          # OPT-13B-shaped W4A8
+    (130, 5120, 264, 16, 4, 4),
+    (64, 9216, 136, 32, 3, 4),          # OPT-66B-shaped W4A3
+    (33, 9216, 128, 32, 4, 4),
+    (1, 512, 72, 4, 4, 8),              # M = 1
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: "M{}K{}N{}g{}A{}W{}".format(*c))
+def test_qgemm_accumulators_bit_exact_and_y(P, case):
+    M, K, N, g, ab, wb = case
+    _say("gemm", case)
+    c = layer_case(M, K, N, g, ab, wb, seed=M + K + N)
+    q, codes = _oracle_codes(c)
+    Y_o, acc_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w, return_acc=True)
+    wp, cs, sw = _gemm_inputs(P, c)
+    acc = torch.full((g, M, N), -7, dtype=torch.int32, device="cuda")
+    Y = P.rptq_qgemm(dev(codes), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs, acc_debug=acc)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_o)
+    assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
+    # the debug buffer does not change Y
+    Y2 = P.rptq_qgemm(dev(codes), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs)
+    assert torch.equal(Y, Y2)
+
+
+@pytest.mark.parametrize("bounds", [[0, 1, 2, 3, 64, 96, 97, 160, 256], [0, 256],
+                                    list(range(0, 65)) + [256]],
+                         ids=["size1", "g1", "g65"])
+@pytest.mark.parametrize("ab,wb", [(3, 4), (4, 4), (8, 8), (8, 4)])
+def test_qgemm_ragged_clusters(P, bounds, ab, wb):
+    if len(bounds) - 1 > 64:
+        bounds = bounds[:64] + [256]                  # g = 64: 63 singletons + one big cluster
+    c = explicit_case(67, 256, 96, bounds, ab, wb, seed=len(bounds) + ab)
+    q, codes = _oracle_codes(c)
+    Y_o, acc_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w, return_acc=True)
+    wp, cs, sw = _gemm_inputs(P, c)
+    acc = torch.zeros((c.g, c.M, c.N), dtype=torch.int32, device="cuda")
+    Y = P.rptq_qgemm(dev(codes), c.M, c.K, c.N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs, acc_debug=acc)
+    assert np.array_equal(acc.cpu().numpy(), acc_o)
+    assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
+
+
+@pytest.mark.parametrize("ab", [3, 4, 8])
+def test_end_to_end_ln_then_gemm(P, ab):
+    M, K, N, g = 150, 2048, 520, 8
+    c = layer_case(M, K, N, g, ab, 4, seed=77 + ab)
+    _, codes_o = _oracle_codes(c)
+    q = orc.unpack_seg32(codes_o, K, c.bounds, ab)
+    Y_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w)
+    codes = _fused(P, c, ab)
+    wp, cs, sw = _gemm_inputs(P, c)
+    Y = P.rptq_qgemm(codes, M, K, N, c.bounds, c.s, c.z, ab, wp, 4, sw, cs)
+    assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
+
+
+# ----------------------------------------------------------------------------- calibration
+def test_calib_minmax_matches_oracle(P):
+    K = 1024
+    mu, sg = synthetic.channel_params(K, 5, 0.01)
+    x = synthetic.tokens(200, mu, sg, 5, synthetic.STREAM_CALIB)
+    x[3, :4] = [-0.0, 0.0, 65504, -65504]
+    gamma, beta = synthetic.ln_params(K, 5)
+    mx, mn = P.rptq_calib_minmax(dev(x.view(np.int16)).view(torch.float16), P.RPTQ_CALIB_RAW)
+    mx_o, mn_o = orc.channel_minmax(x)
+    assert np.array_equal(mx.cpu().numpy(), mx_o) and np.array_equal(mn.cpu().numpy(), mn_o)
+    mx, mn = P.rptq_calib_minmax(dev(x.view(np.int16)).view(torch.float16), P.RPTQ_IN_FP16_RAW,
+                                 dev(gamma), dev(beta))
+    mx_o, mn_o = orc.channel_minmax(orc.layernorm(x, gamma, beta))
+    np.testing.assert_allclose(mx.cpu().numpy(), mx_o, rtol=2e-5, atol=2e-5)
+    np.testing.assert_allclose(mn.cpu().numpy(), mn_o, rtol=2e-5, atol=2e-5)
