@@ -70,9 +70,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-kv", action="store_true", help="skip the K/V cache kernels (profiling runs)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle baseline leg (0: leave it out)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: every box in this setup has a single MI355X and the "
@@ -124,7 +123,7 @@ def main():
     kvw = synthetic.KV_WORKLOADS["opt66b_kv_a3"]
     T, C, kvb = kvw.T, kvw.C, kvw.bits
     kv = {}
-    if not args.no_kv:
+    if True:
         for name, (s_ch, s_cal, s_ev) in {"K": (synthetic.STREAM_CHANNELS, synthetic.STREAM_CALIB,
                                                 synthetic.STREAM_EVAL),
                                           "V": (synthetic.STREAM_CHANNELS_V, synthetic.STREAM_CALIB_V,
@@ -144,7 +143,7 @@ def main():
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ one step
-    names = ["ln4", "gemm4", "ln3", "gemm3"] + ([] if args.no_kv else ["kvq_K", "kvq_V", "kvd_K", "kvd_V"])
+    names = ["ln4", "gemm4", "ln3", "gemm3", "kvq_K", "kvq_V", "kvd_K", "kvd_V"]
 
     def step(ev=None):
         def rec(i):
@@ -160,7 +159,7 @@ def main():
                          stream=stream)
             k += 2
         rec(k)
-        if not args.no_kv:
+        if True:
             for name in ("K", "V"):
                 d = kv[name]
                 P.rptq_kv_quant_pack(d["x"], d["R"], d["bounds"], d["s"], d["z"], kvb, out=d["packed"], stream=stream)
@@ -202,7 +201,7 @@ def main():
                              gemm_tops=ops / t_gm / 1e12, gemm_frac_int8_peak=ops / t_gm / 1e12 / INT8_PEAK_TOPS,
                              ln_GBps=ln_bytes / t_ln / 1e9, ln_frac_hbm_peak=ln_bytes / t_ln / 1e9 / HBM_PEAK_GBPS)
     out = {}
-    if not args.no_kv:
+    if True:
         kv_bytes = T * C * (2 + kvb / 8)
         tq = (avg["kvq_K"] + avg["kvq_V"]) / 2
         td = (avg["kvd_K"] + avg["kvd_V"]) / 2
@@ -223,14 +222,14 @@ def main():
                  {"bound": "hbm", "kernel": "ln_reorder_quant_kernel<4,0>", "achieved": ln_bytes / avg["ln4"] / 1e9,
                   "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ln_bytes / avg["ln4"] / 1e9 / HBM_PEAK_GBPS,
                   "traffic": measured_traffic("ln_reorder_quant", ln_bytes)}]
-    if not args.no_kv:
+    if True:
         rooflines.append({"bound": "hbm", "kernel": "kv_quant_pack_kernel<3>", "achieved": out["kv_pack_GBps"],
                           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": out["kv_pack_frac_hbm_peak"],
                           "traffic": measured_traffic("kv_quant_pack", T * C * (2 + kvb / 8))})
 
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
-    if not args.no_cpu:
+    if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, x, gamma, beta, R, bounds, variants[4]["s"], variants[4]["z"], N, args.cpu_seconds)
 
     line = {

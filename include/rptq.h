@@ -135,8 +135,8 @@ int rptq_ln_reorder_quant(const void* x, int32_t in_mode, int64_t M, int32_t K,
  * s_w      device fp32 [N];  colsum device int32 [g][N].
  * Y        device fp32 [M][N], row-major.
  * acc_debug device int32 [g][M][N] or NULL: receives every acc_c (validation).
- * Limits: N % 8 == 0 (RPTQ_ERR_UNSUPPORTED); every |acc_c| must fit int32
- * (always true for K <= RPTQ_MAX_K).
+ * Limits: K <= RPTQ_MAX_K (RPTQ_ERR_UNSUPPORTED), which also keeps every
+ * |acc_c| within int32; any M >= 0 and N >= 1.
  */
 int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N,
                const int32_t* bounds, int32_t g, const float* s, const int32_t* z, int32_t a_bits,
@@ -161,7 +161,8 @@ int rptq_kv_quant_pack(const uint16_t* kv, int64_t T, int32_t C, const int32_t* 
 /*
  * K/V-cache dequantize, back to natural channel order (quantization lecture
  * 1.3: W = S (Wq - Z)):
- *   out[t][R[j]] = fp16_rne( fp32( s_c * (q[t][j] - z_c) ) )
+ *   out[t][R[j]] = fp16_rne( s_c * (q[t][j] - z_c) )
+ * the product taken exactly and rounded once to fp16, half to even.
  * packed   device uint8 [T][C*bits/8] (DENSE, from rptq_kv_quant_pack).
  * out      device fp16 [T][C].  Other arguments and limits as rptq_kv_quant_pack.
  */

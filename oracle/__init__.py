@@ -60,6 +60,7 @@ def _declare(L):
         "orc_num_threads": (ctypes.c_int, []),
         "orc_half_to_double": (ctypes.c_double, [ctypes.c_uint16]),
         "orc_float_to_half": (ctypes.c_uint16, [_F]),
+        "orc_double_to_half": (ctypes.c_uint16, [ctypes.c_double]),
         "orc_half_to_double_array": (None, [_P, _I64, _P]),
         "orc_float_to_half_array": (None, [_P, _I64, _P]),
         "orc_layernorm": (None, [_P, _I64, _I32, _P, _P, _F, _P, _P]),

@@ -63,11 +63,12 @@ double orc_half_to_double(uint16_t h) {
     return sign ? -v : v;
 }
 
-// Round-to-nearest-even conversion of a binary32 value to binary16.
-uint16_t orc_float_to_half(float x) {
+// Round-to-nearest-even conversion to binary16 of a value held exactly in a
+// double (one rounding).
+uint16_t orc_double_to_half(double x) {
     const uint16_t sign = std::signbit(x) ? 0x8000 : 0;
     if (std::isnan(x)) return sign | 0x7e00;
-    const double a = std::fabs((double)x);
+    const double a = std::fabs(x);
     // 65504 is the largest finite half; the midpoint to the next binade step
     // (65536) is 65520, which ties to the even neighbour: infinity.
     if (a >= 65520.0) return sign | 0x7c00;
@@ -84,6 +85,9 @@ uint16_t orc_float_to_half(float x) {
     if (r == 2048.0) { r = 1024.0; E += 1; }
     return sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)r - 1024);
 }
+
+// Round-to-nearest-even conversion of a binary32 value to binary16.
+uint16_t orc_float_to_half(float x) { return orc_double_to_half((double)x); }
 
 void orc_half_to_double_array(const uint16_t* h, int64_t n, double* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_half_to_double(h[i]);
@@ -603,7 +607,8 @@ int orc_qgemm(const uint8_t* q, int64_t M, int32_t K, const int8_t* Wq, const in
 // kv: [T][C] fp16, natural channel order.  Codes are produced in reordered
 // order (position j reads channel R[j]) and DENSE-packed.
 // Dequantization writes fp16 back in natural order:
-//   out[t][R[j]] = fp16_rne( fp32( s_c * (q - z_c) ) )
+//   out[t][R[j]] = fp16_rne( s_c * (q - z_c) )
+// with the product formed exactly (fp64) and rounded once, half to even.
 // ---------------------------------------------------------------------------
 int orc_kv_quant_pack(const uint16_t* kv, int64_t T, int32_t C, const int32_t* R,
                       const int32_t* bounds, int32_t g, const float* s, const int32_t* z,
@@ -638,8 +643,8 @@ int orc_kv_dequant(const uint8_t* packed, int64_t T, int32_t C, const int32_t* R
         for (int32_t j = 0; j < C; ++j) {
             const int32_t c = cluster_of(bounds, g, j);
             const int32_t k = R ? R[j] : j;
-            const float v = s[c] * (float)((int32_t)q[j] - z[c]);
-            out[t * (int64_t)C + k] = orc_float_to_half(v);
+            const double v = (double)s[c] * (double)((int32_t)q[j] - z[c]);   // exact
+            out[t * (int64_t)C + k] = orc_double_to_half(v);
         }
     }
     return bad ? -1 : 0;

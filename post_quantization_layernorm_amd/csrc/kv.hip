@@ -149,10 +149,10 @@ __global__ __launch_bounds__(kBlock) void kv_dequant_kernel(
             load_unit<BITS>(prow, unit, q);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                // (q - z) is an exact integer in fp32; one rounding for the
-                // product, one for the conversion to fp16 (round to nearest even)
-                const float v = sc[u][e] * ((float)q[e] - zf[u][e]);
-                *reinterpret_cast<_Float16*>(orow + dst[u][e]) = (_Float16)v;
+                // (q - z) is an exact integer in fp32; the product is rounded
+                // once, straight to fp16 (v_fma_mixlo_f16: fused, half to even)
+                const float d = (float)q[e] - zf[u][e];
+                *reinterpret_cast<_Float16*>(orow + dst[u][e]) = (_Float16)(sc[u][e] * d);
             }
         }
         __syncthreads();

@@ -10,22 +10,32 @@
 //   Y[m][n] = s_w[n] * sum_c s_c * (acc_c[m][n] - z_c * colsum_c[n]),
 //   acc_c   = sum over the cluster's K-segment of q * W'   (int32, exact).
 //
-// Design:
-//   - 128 x 128 output tile per 256-thread workgroup, 2 x 2 waves of 64 x 64,
-//     each wave 2 x 2 v_mfma_i32_32x32x32_i8 tiles;
-//   - K advances in stages of 64 codes (two MFMA steps of 32); every cluster
-//     is padded to a multiple of 32 codes, so a step never straddles clusters;
-//   - A (3/4/8-bit activation codes) and W' (4/8-bit weights) are read from
-//     global memory packed, unpacked to int8 in registers, and staged in a
-//     double-buffered LDS tile (row stride 80 B: conflict-free 16-B fragment
-//     reads); the next stage's global loads are in flight during the MFMAs;
-//   - the int32 accumulators hold one cluster at a time: at the cluster's
-//     last step they are converted and scaled into fp32 accumulators
-//     (out += s_c * acc) and restart at zero;
-//   - 8-bit codes q are staged as q - 128 (signed int8 MFMA) and 4-bit
-//     weights as 16 * w (nibble placed in the high half of the byte, so the
-//     sign comes for free); both are undone exactly in the scale / epilogue:
-//     corr[n] = sum_c s_c (z_c - offset) colsum_c[n] in fp64.
+// Design (one 512-thread workgroup per CU, 8 waves, 2 per SIMD so one wave's
+// VALU work overlaps the other's MFMAs):
+//   - 256 x 128 output tile, waves in a 4 x 2 grid of 64 x 64, each wave a
+//     2 x 2 grid of v_mfma_i32_32x32x32_i8 tiles;
+//   - K advances in stages of 128 codes (4 MFMA steps of 32).  Clusters are
+//     padded to multiples of 32 codes, so a step never straddles clusters;
+//   - A (3/4/8-bit activation codes) and W' (4/8-bit weights) are fetched
+//     packed with buffer loads (scalar stage offsets; rows past M or N read
+//     as zero), two stages ahead of the MFMAs, unpacked to int8 in registers
+//     and staged in a double-buffered LDS tile (row stride 144 B: the 16-byte
+//     fragment reads of 8 consecutive lanes hit disjoint banks);
+//   - one running int32 accumulator per MFMA tile for the whole K loop: at
+//     the last step of cluster c it is converted and added to fp32 out with
+//     weight d_c = s_c - s_(c+1) (summation by parts of sum_c s_c acc_c), so
+//     the accumulators are never reset and every step is the same code;
+//   - the next stage's staging (unpack + LDS store of one piece per step) is
+//     interleaved with the current stage's MFMAs: LDS stores are the scarce
+//     LDS resource on gfx950 (~75 B/clk/CU against ~220 B/clk/CU for
+//     16-byte reads);
+//   - 8-bit codes q are staged as q - 128 (signed MFMA operands) and 4-bit
+//     weights as 16 * w (nibble moved to the high half of the byte, sign for
+//     free); both are undone exactly: s_c / 16 in the scale, and
+//     corr[n] = sum_c s_c (z_c - offset) colsum_c[n] (fp64) in the epilogue;
+//   - workgroups are numbered so that consecutive tiles of a group land on
+//     the same XCD (the dispatcher deals workgroups round-robin over the 8
+//     XCDs), sharing its L2.
 #include "rptq_device.hpp"
 
 namespace rptq {
@@ -33,23 +43,30 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
-constexpr int BM = 128, BN = 128, BKS = 64, LDSS = 80;
+constexpr int GROUP_M = 8;
+constexpr uint32_t kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
 
-// 32 codes of ABITS bits = ABITS 32-bit words, starting 4-byte aligned.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
+    const int32_t n = bytes <= 0 ? 0 : bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, kRsrcWord3);
+}
+
+// One 32-code piece of BITS-bit codes = BITS 32-bit words.
 template <int BITS>
-__device__ __forceinline__ void load_codes(const uint8_t* p, bool ok, uint32_t (&d)[BITS]) {
-    if constexpr (BITS == 4) {
-        uint4 v = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t (&d)[BITS]) {
+    if constexpr (BITS == 3) {
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, 0);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z;
+    } else if constexpr (BITS == 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
         d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-    } else if constexpr (BITS == 8) {
-        uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-        if (ok) { v0 = reinterpret_cast<const uint4*>(p)[0]; v1 = reinterpret_cast<const uint4*>(p)[1]; }
+    } else {
+        const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+        const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0);
         d[0] = v0.x; d[1] = v0.y; d[2] = v0.z; d[3] = v0.w;
         d[4] = v1.x; d[5] = v1.y; d[6] = v1.z; d[7] = v1.w;
-    } else {
-        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-        d[0] = ok ? q[0] : 0u; d[1] = ok ? q[1] : 0u; d[2] = ok ? q[2] : 0u;
     }
 }
 
@@ -91,51 +108,111 @@ __device__ __forceinline__ void unpack_wgt(const uint32_t (&d)[BITS], uint32_t (
 }
 
 __device__ __forceinline__ void store32(int8_t* lds, const uint32_t (&o)[8]) {
-    reinterpret_cast<uint4*>(lds)[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    reinterpret_cast<uint4*>(lds)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    reinterpret_cast<u32x4*>(lds)[0] = u32x4{o[0], o[1], o[2], o[3]};
+    reinterpret_cast<u32x4*>(lds)[1] = u32x4{o[4], o[5], o[6], o[7]};
 }
 
-template <int ABITS, int WBITS>
-__global__ __launch_bounds__(256, 2) void qgemm_kernel(
-    const uint8_t* __restrict__ A, int64_t M, int64_t a_row_bytes,
-    const uint8_t* __restrict__ B, int32_t N, int64_t b_row_bytes,
+// Tile configuration: BM x BN output tile, WAVES waves in a (BM/64) x (BN/64)
+// grid of 64 x 64 wave tiles, SK 32-code steps per pipeline stage, MINBLK
+// resident workgroups per CU.
+template <int BM_, int BN_, int WAVES_, int SK_, int MINBLK_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, WAVES = WAVES_, SK = SK_, MINBLK = MINBLK_;
+    static constexpr int NT = WAVES * 64, WN = BN / 64;
+    static constexpr int LDSS = SK * 32 + 16;          // LDS row stride (bytes)
+    static constexpr int PA = BM * SK / NT, PB = BN * SK / NT;   // pieces per thread
+    static_assert((BM / 64) * (BN / 64) == WAVES, "one 64x64 tile per wave");
+    static_assert(PA * NT == BM * SK && PB * NT == BN * SK && PA >= 1 && PB >= 1, "staging split");
+};
+
+template <int ABITS, int WBITS, int PA, int PB>
+struct StageRegs {
+    uint32_t a[PA][ABITS], b[PB][WBITS];
+};
+
+template <int ABITS, int WBITS, bool DEBUG, class CFG>
+__global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
+    const uint8_t* __restrict__ A, int64_t M, int32_t a_row_bytes,
+    const uint8_t* __restrict__ B, int32_t N, int32_t b_row_bytes,
     const GemmArgs ga, const float* __restrict__ s_w, const int32_t* __restrict__ colsum,
-    float* __restrict__ Y, int32_t* __restrict__ acc_dbg) {
+    float* __restrict__ Y, int32_t* __restrict__ acc_dbg, int32_t tiles_m, int32_t tiles_n) {
+    constexpr int BM = CFG::BM, BN = CFG::BN, SK = CFG::SK, LDSS = CFG::LDSS, NT = CFG::NT;
+    constexpr int PA = CFG::PA, PB = CFG::PB, WN = CFG::WN;
+    constexpr int NPIECE = PA + PB;
+    static_assert(NPIECE <= SK, "one staged piece per step");
     __shared__ __align__(16) int8_t As[2][BM * LDSS];
     __shared__ __align__(16) int8_t Bs[2][BN * LDSS];
+    constexpr int APIECE = 4 * ABITS, BPIECE = 4 * WBITS;           // bytes per 32 codes
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wm = wid >> 1, wn = wid & 1;
-    const int tiles_n = (N + BN - 1) / BN;
-    const int64_t bm = blockIdx.x / tiles_n;
-    const int bn = blockIdx.x % tiles_n;
-    const int64_t m0 = bm * BM;
+    // ---- tile of this workgroup: undo the round-robin XCD dealing, then a
+    // grouped (GROUP_M tile-rows at a time) column-major walk
+    const int total = tiles_m * tiles_n;
+    const int wg = blockIdx.x, xcd = wg & 7, q8 = total >> 3, r8 = total & 7;
+    const int logical = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + (wg >> 3);
+    const int per_group = GROUP_M * tiles_n;
+    const int first_m = (logical / per_group) * GROUP_M;
+    const int gsize = min(tiles_m - first_m, GROUP_M);
+    const int bm = first_m + (logical % per_group) % gsize;
+    const int bn = (logical % per_group) / gsize;
+    const int64_t m0 = (int64_t)bm * BM;
     const int n0 = bn * BN;
 
-    // global -> LDS staging: thread owns row `lr`, codes [32*part, 32*part+32) of a stage
-    const int lr = tid >> 1, part = tid & 1;
-    const bool a_row_ok = m0 + lr < M;
-    const bool b_row_ok = n0 + lr < N;
-    const uint8_t* a_ptr = A + (a_row_ok ? (m0 + lr) * a_row_bytes : 0) + part * (32 * ABITS / 8);
-    const uint8_t* b_ptr = B + (b_row_ok ? (int64_t)(n0 + lr) * b_row_bytes : 0) + part * (32 * WBITS / 8);
-    constexpr int ASTAGE = BKS * ABITS / 8, BSTAGE = BKS * WBITS / 8;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid / WN, wn = wid % WN;
+
+    // ---- staging: piece p = tid + i * NT covers row p / SK, step p % SK of a stage
+    uint32_t a_voff[PA], b_voff[PB];
+    int a_lds[PA], b_lds[PB], a_step[PA], b_step[PB];
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+        const int p = tid + i * NT, row = p / SK, part = p % SK;
+        a_voff[i] = (uint32_t)(row * a_row_bytes + part * APIECE);
+        a_lds[i] = row * LDSS + part * 32;
+        a_step[i] = part;
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+        const int p = tid + i * NT, row = p / SK, part = p % SK;
+        b_voff[i] = (uint32_t)(row * b_row_bytes + part * BPIECE);
+        b_lds[i] = row * LDSS + part * 32;
+        b_step[i] = part;
+    }
+    const uint8_t* a_tile = A + m0 * a_row_bytes;
+    const uint8_t* b_tile = B + (int64_t)n0 * b_row_bytes;
+    const int64_t a_left = (M - m0) * a_row_bytes;
+    const int64_t b_left = (int64_t)(N - n0) * b_row_bytes;
     const int nsteps = ga.nsteps;
-    const int nstages = (nsteps + 1) / 2;
+    const int nst = (nsteps + SK - 1) / SK;
 
-    uint32_t ra[ABITS], rb[WBITS];
-    auto gload = [&](int st) {
-        const bool in_k = 2 * st + part < nsteps;
-        load_codes<ABITS>(a_ptr + (int64_t)st * ASTAGE, a_row_ok && in_k, ra);
-        load_codes<WBITS>(b_ptr + (int64_t)st * BSTAGE, b_row_ok && in_k, rb);
+    // Pieces of steps past the end of K read as zero (offset beyond the
+    // buffer), so the MFMAs of a partial last stage add nothing.
+    using Stage = StageRegs<ABITS, WBITS, PA, PB>;
+    auto gload = [&](Stage& S, int st) {
+        const int64_t ao = (int64_t)st * (SK * APIECE), bo = (int64_t)st * (SK * BPIECE);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile + ao, a_left - ao);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile + bo, b_left - bo);
+        const int room = nsteps - st * SK;
+#pragma unroll
+        for (int i = 0; i < PA; ++i) load_piece<ABITS>(ra, a_step[i] < room ? a_voff[i] : 0x80000000u, S.a[i]);
+#pragma unroll
+        for (int i = 0; i < PB; ++i) load_piece<WBITS>(rb, b_step[i] < room ? b_voff[i] : 0x80000000u, S.b[i]);
     };
-    auto lstore = [&](int buf) {
+    // stage piece k of register set S into LDS buffer buf
+    auto put = [&](const Stage& S, int buf, int k) {
         uint32_t o[8];
-        unpack_act<ABITS>(ra, o);
-        store32(&As[buf][lr * LDSS + part * 32], o);
-        unpack_wgt<WBITS>(rb, o);
-        store32(&Bs[buf][lr * LDSS + part * 32], o);
+        if (k < PA) {
+            unpack_act<ABITS>(S.a[k], o);
+            store32(&As[buf][a_lds[k]], o);
+        } else {
+            unpack_wgt<WBITS>(S.b[k - PA], o);
+            store32(&Bs[buf][b_lds[k - PA]], o);
+        }
     };
 
+    // One running int32 accumulator per MFMA tile over the whole K loop, and
+    // fp32 out.  With A_c the running sum at the end of cluster c,
+    //   sum_c s_c (A_c - A_(c-1)) = sum_c (s_c - s_(c+1)) A_c,  s_(g+1) = 0,
+    // so at each cluster end out += d_c * A_c and nothing is reset.
     v16i acc[2][2];
     float out[2][2][16];
 #pragma unroll
@@ -146,73 +223,121 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) out[i][j][r] = 0.0f;
         }
-
-    // output coordinates of this lane's accumulator registers
-    const int row_in_tile = (lane >> 5) * 4;      // + (r / 4) * 8 + (r % 4)
-    const int col_in_tile = lane & 31;
-
-    int c = 0;
-    int c_end = ga.step_end[0];
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int st = 0; st < nstages; ++st) {
-        const int cur = st & 1;
-        if (st + 1 < nstages) gload(st + 1);
+    [[maybe_unused]] v16i prev[2][2];
+    if constexpr (DEBUG) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int step = 2 * st + ks;
-            if (step >= nsteps) break;
-            v4i af[2], bf[2];
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) prev[i][j] = (v16i)0;
+    }
+
+    // accumulator register r of this lane holds row (r/4)*8 + (lane/32)*4 + r%4, column lane%32
+    const int row_l = (lane >> 5) * 4, col_l = lane & 31;
+    const int a_frag = (wm * 64 + (lane & 31)) * LDSS + (lane >> 5) * 16;
+    const int b_frag = (wn * 64 + (lane & 31)) * LDSS + (lane >> 5) * 16;
+
+    // cluster tables held one entry per lane (g <= 64) and read with readlane:
+    // no scalar memory loads (and their waits) inside the K loop
+    const int lane_c = lane < ga.g ? lane : ga.g - 1;
+    const int end_l = ga.step_end[lane_c];
+    const float d_l = ga.scale[lane_c];
+    int c = 0, c_end = __builtin_amdgcn_readfirstlane(end_l);
+
+    auto flush = [&](int cl) {
+        const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d_l), cl));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    out[i][j][r] = __builtin_fmaf(d, (float)acc[i][j][r], out[i][j][r]);
+                if constexpr (DEBUG) {
+                    const int n = n0 + wn * 64 + j * 32 + col_l;
+                    const int add = (n < N && ga.code_offset) ? ga.code_offset * colsum[(int64_t)cl * N + n] : 0;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+                        const int v = acc[i][j][r] - prev[i][j][r];
+                        if (m < M && n < N)
+                            acc_dbg[((int64_t)cl * M + m) * N + n] = (WBITS == 4 ? (v >> 4) : v) + add;
+                    }
+                    prev[i][j] = acc[i][j];
+                }
+            }
+    };
+
+    // One stage: 4 MFMA steps from LDS buffer `buf`; the fragments of step
+    // ks + 1 are read before the MFMAs of step ks, and piece ks of the next
+    // stage's staging registers `nxt` is unpacked into the other buffer in
+    // the same instruction stream (on the last stage that buffer is never
+    // read again, so the stores are harmless).
+    auto compute = [&](int buf, int st, const Stage& nxt) {
+        v4i af[2][2], bf[2][2];
+        auto rd = [&](int slot, int ks) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const v4i*>(
-                    &As[cur][(wm * 64 + i * 32 + (lane & 31)) * LDSS + ks * 32 + (lane >> 5) * 16]);
+                af[slot][i] = *reinterpret_cast<const v4i*>(&As[buf][a_frag + i * 32 * LDSS + ks * 32]);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                bf[j] = *reinterpret_cast<const v4i*>(
-                    &Bs[cur][(wn * 64 + j * 32 + (lane & 31)) * LDSS + ks * 32 + (lane >> 5) * 16]);
+                bf[slot][j] = *reinterpret_cast<const v4i*>(&Bs[buf][b_frag + j * 32 * LDSS + ks * 32]);
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < SK; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < SK) rd(cur ^ 1, ks + 1);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-            if (step + 1 == c_end) {
-                const float sc = ga.scale[c];
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            out[i][j][r] = __builtin_fmaf(sc, (float)acc[i][j][r], out[i][j][r]);
-                        if (acc_dbg) {
-                            const int n = n0 + wn * 64 + j * 32 + col_in_tile;
-                            const int add = (n < N && ga.code_offset) ? ga.code_offset * colsum[(int64_t)c * N + n] : 0;
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int64_t m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + row_in_tile + (r & 3);
-                                if (m < M && n < N) {
-                                    const int v = WBITS == 4 ? (acc[i][j][r] >> 4) : acc[i][j][r];
-                                    acc_dbg[((int64_t)c * M + m) * N + n] = v + add;
-                                }
-                            }
-                        }
-                        acc[i][j] = (v16i)0;
-                    }
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
+            if (ks < NPIECE) put(nxt, buf ^ 1, ks);    // unused on the last stage
+            // issue order inside the step: each MFMA is followed by part of
+            // the next step's fragment reads, the unpack VALU work, and last
+            // the staging stores (so the reads never wait behind them)
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            if (st * SK + ks + 1 == c_end) {
+                flush(c);
                 ++c;
-                c_end = c < ga.g ? ga.step_end[c] : 0x7fffffff;
+                c_end = c < ga.g ? __builtin_amdgcn_readlane(end_l, c) : 0x7fffffff;
             }
         }
-        if (st + 1 < nstages) lstore(cur ^ 1);
+    };
+
+    // ---- pipeline: register set R[st & 1] is free at the start of stage st
+    // and receives stage st + 2; R[(st + 1) & 1] holds stage st + 1, which is
+    // unpacked into LDS during stage st.  One barrier per stage.
+    Stage R0, R1;
+    gload(R0, 0);
+    if (nst > 1) gload(R1, 1);
+#pragma unroll
+    for (int k = 0; k < NPIECE; ++k) put(R0, 0, k);
+    __syncthreads();
+    for (int st = 0; st < nst; st += 2) {
+        if (st + 2 < nst) gload(R0, st + 2);
+        compute(0, st, R1);
+        __syncthreads();
+        if (st + 1 >= nst) break;
+        if (st + 3 < nst) gload(R1, st + 3);
+        compute(1, st + 1, R0);
         __syncthreads();
     }
 
-    // epilogue: Y = s_w * (out - corr), corr[n] = sum_c s_c (z_c - offset) colsum_c[n]
+    // ---- epilogue: Y = s_w * (out - corr), corr[n] = sum_c s_c (z_c - offset) colsum_c[n]
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + col_in_tile;
+        const int n = n0 + wn * 64 + j * 32 + col_l;
         if (n >= N) continue;
         double corr = 0.0;
         for (int cc = 0; cc < ga.g; ++cc) corr += ga.sz[cc] * (double)colsum[(int64_t)cc * N + n];
@@ -221,15 +346,22 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + row_in_tile + (r & 3);
-                if (m < M) Y[m * N + n] = (float)(sw * ((double)out[i][j][r] - corr));
+                const int64_t m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+                if (m < M) __builtin_nontemporal_store((float)(sw * ((double)out[i][j][r] - corr)), Y + m * N + n);
             }
     }
 }
 
+using Cfg = TileCfg<256, 128, 8, 4, 1>;
+
+template <int ABITS, int WBITS>
+const void* pick2(bool debug) {
+    return debug ? (const void*)qgemm_kernel<ABITS, WBITS, true, Cfg> : (const void*)qgemm_kernel<ABITS, WBITS, false, Cfg>;
+}
+
 template <int ABITS>
-const void* pick(int wbits) {
-    return wbits == 4 ? (const void*)qgemm_kernel<ABITS, 4> : (const void*)qgemm_kernel<ABITS, 8>;
+const void* pick(int wbits, bool debug) {
+    return wbits == 4 ? pick2<ABITS, 4>(debug) : pick2<ABITS, 8>(debug);
 }
 
 }  // namespace
@@ -238,13 +370,16 @@ hipError_t launch_qgemm(const uint8_t* codes, int64_t M, int32_t N, int64_t a_ro
                         int a_bits, const uint8_t* w_packed, int64_t w_row_bytes, int w_bits,
                         const GemmArgs& ga, const float* s_w, const int32_t* colsum,
                         float* Y, int32_t* acc_debug, hipStream_t stream) {
-    const void* k = a_bits == 3 ? pick<3>(w_bits) : a_bits == 4 ? pick<4>(w_bits) : pick<8>(w_bits);
-    const int64_t tiles = ((M + BM - 1) / BM) * (int64_t)((N + BN - 1) / BN);
-    if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-    void* args[] = {(void*)&codes, (void*)&M, (void*)&a_row_bytes, (void*)&w_packed, (void*)&N,
-                    (void*)&w_row_bytes, (void*)&ga, (void*)&s_w, (void*)&colsum, (void*)&Y,
-                    (void*)&acc_debug};
-    return hipLaunchKernel(k, dim3((unsigned)tiles), dim3(256), args, 0, stream);
+    const bool dbg = acc_debug != nullptr;
+    const void* k = a_bits == 3 ? pick<3>(w_bits, dbg) : a_bits == 4 ? pick<4>(w_bits, dbg) : pick<8>(w_bits, dbg);
+    const int64_t tm = (M + Cfg::BM - 1) / Cfg::BM, tn = (N + Cfg::BN - 1) / Cfg::BN;
+    if (tm * tn > 0x7fffffff || a_row_bytes > (1 << 20) || w_row_bytes > (1 << 20)) return hipErrorInvalidValue;
+    int32_t tiles_m = (int32_t)tm, tiles_n = (int32_t)tn;
+    int32_t arb = (int32_t)a_row_bytes, wrb = (int32_t)w_row_bytes;
+    void* args[] = {(void*)&codes, (void*)&M, (void*)&arb, (void*)&w_packed, (void*)&N, (void*)&wrb,
+                    (void*)&ga, (void*)&s_w, (void*)&colsum, (void*)&Y, (void*)&acc_debug,
+                    (void*)&tiles_m, (void*)&tiles_n};
+    return hipLaunchKernel(k, dim3((unsigned)(tm * tn)), dim3(Cfg::NT), args, 0, stream);
 }
 
 }  // namespace rptq

@@ -217,8 +217,13 @@ int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N, const int3
     for (int c = 0; c < g; ++c) {
         steps += (bounds[c + 1] - bounds[c] + 31) / 32;
         ga.step_end[c] = steps;
-        ga.scale[c] = w_bits == 4 ? s[c] * 0.0625f : s[c];     // 4-bit weights staged as 16*w
         ga.sz[c] = (double)s[c] * ((double)z[c] - (double)ga.code_offset);
+    }
+    // flush weights of the running accumulator: d_c = s_c - s_(c+1), s_(g+1) = 0
+    // (4-bit weights are staged as 16 * w, hence the 1/16)
+    for (int c = 0; c < g; ++c) {
+        const double d = (double)s[c] - (c + 1 < g ? (double)s[c + 1] : 0.0);
+        ga.scale[c] = (float)(w_bits == 4 ? d * 0.0625 : d);
     }
     ga.nsteps = steps;
     const int64_t a_row_bytes = (int64_t)steps * 32 * a_bits / 8;

@@ -35,7 +35,7 @@ struct GemmArgs {
     int32_t g;
     int32_t nsteps;                        // K_pad / 32
     int32_t step_end[kMaxClusters];        // exclusive end (in 32-code steps) of cluster c
-    float scale[kMaxClusters];             // s_c divided by the weight pre-scale
+    float scale[kMaxClusters];             // (s_c - s_(c+1)) divided by the weight pre-scale
     double sz[kMaxClusters];               // s_c * (z_c - code offset), for the epilogue
     int32_t code_offset;                   // 128 for 8-bit activations (stored q - 128), else 0
 };
