@@ -29,7 +29,7 @@ __device__ __forceinline__ void atomic_fmin(float* addr, float v) {
 }
 
 template <bool LN>
-__global__ __launch_bounds__(kBlock) void calib_kernel(const uint16_t* __restrict__ x, int64_t M,
+__global__ __launch_bounds__(kCalibBlock) void calib_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                        int32_t K, const float* __restrict__ gamma,
                                                        const float* __restrict__ beta, float eps,
                                                        float* __restrict__ mx, float* __restrict__ mn) {
@@ -40,11 +40,11 @@ __global__ __launch_bounds__(kBlock) void calib_kernel(const uint16_t* __restric
     float mean = 0.0f, rstd = 1.0f;
     if constexpr (LN) {
         float s = 0.0f;
-        for (int k = threadIdx.x; k < K; k += kBlock) s += (float)xr[k];
+        for (int k = threadIdx.x; k < K; k += kCalibBlock) s += (float)xr[k];
         s = block_sum_256(s, red);
         mean = s / (float)K;
         float ss = 0.0f;
-        for (int k = threadIdx.x; k < K; k += kBlock) {
+        for (int k = threadIdx.x; k < K; k += kCalibBlock) {
             const float d = (float)xr[k] - mean;
             ss = __builtin_fmaf(d, d, ss);
         }
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kBlock) void calib_kernel(const uint16_t* __restric
         rstd = 1.0f / __builtin_sqrtf(ss / (float)K + eps);
     }
     const float nmr = -mean * rstd;
-    for (int k = threadIdx.x; k < K; k += kBlock) {
+    for (int k = threadIdx.x; k < K; k += kCalibBlock) {
         float v = (float)xr[k];
         if constexpr (LN) v = __builtin_fmaf(gamma[k], __builtin_fmaf(v, rstd, nmr), beta[k]);
         v += 0.0f;                      // -0 -> +0 so the integer orders agree
@@ -68,9 +68,9 @@ hipError_t launch_calib_minmax(const uint16_t* x, int mode, int64_t M, int32_t K
                                float* mx, float* mn, hipStream_t stream) {
     fill_kernel<<<dim3((K + 255) / 256), dim3(256), 0, stream>>>(mx, mn, K);
     if (mode == RPTQ_IN_FP16_RAW)
-        calib_kernel<true><<<dim3((unsigned)M), dim3(kBlock), 0, stream>>>(x, M, K, gamma, beta, eps, mx, mn);
+        calib_kernel<true><<<dim3((unsigned)M), dim3(kCalibBlock), 0, stream>>>(x, M, K, gamma, beta, eps, mx, mn);
     else
-        calib_kernel<false><<<dim3((unsigned)M), dim3(kBlock), 0, stream>>>(x, M, K, gamma, beta, eps, mx, mn);
+        calib_kernel<false><<<dim3((unsigned)M), dim3(kCalibBlock), 0, stream>>>(x, M, K, gamma, beta, eps, mx, mn);
     return hipGetLastError();
 }
 

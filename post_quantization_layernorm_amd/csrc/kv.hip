@@ -9,40 +9,46 @@
 // A persistent workgroup walks the rows; every lane owns fixed units of 8
 // codes (their source/destination channel and cluster constants live in
 // registers), rows are staged in LDS so the R permutation is an LDS gather
-// (quant-pack) or scatter (dequant), and HBM sees only 16-byte coalesced
-// loads and stores.  The next row's loads are issued before the current row
-// is processed.
+// (quant-pack) or scatter (dequant), and HBM sees only coalesced buffer loads
+// and stores.  Two register buffers keep two rows per workgroup in flight
+// while one is processed.  Every memory instruction runs unconditionally
+// with a compile-time count (the buffer range check zero-fills / drops what
+// lies past a row; idle units write a dummy LDS slot), so the compiler's
+// memory-counter waits never cover the next row's loads.
 #include "rptq_device.hpp"
 
 namespace rptq {
 namespace {
 
-__host__ __device__ constexpr int align16(int64_t b) { return (int)((b + 15) & ~int64_t(15)); }
-
-template <int BITS, int UPL>
-__global__ __launch_bounds__(kBlock) void kv_quant_pack_kernel(
+template <int BITS, int UPL, bool OVEC16>
+__global__ __launch_bounds__(kMaxBlock) void kv_quant_pack_kernel(
     const uint16_t* __restrict__ kv, int64_t T, int32_t C, const int32_t* __restrict__ R,
     const ClusterArgs ca, uint8_t* __restrict__ packed) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int QMAX = (1 << BITS) - 1;
-    constexpr int CH = (kMaxK * 2 / 16 + kBlock - 1) / kBlock;
+    constexpr int CH = UPL;                                   // fp16 row: C/8 chunks = C/8 units
+    constexpr int OCH = chunks_for<OVEC16>(UPL * BITS);       // packed row: C*BITS/8 bytes
+    constexpr int OCB = OVEC16 ? 16 : 4;
+    const int BLOCK = blockDim.x;
+    const int64_t in_bytes = (int64_t)C * 2;
     const int64_t row_bytes = (int64_t)C * BITS / 8;
-    unsigned char* xrow = smem;
-    unsigned char* orow = smem + align16((int64_t)C * 2);
+    unsigned char* xrow = smem;                               // CH * 16 * BLOCK bytes
+    unsigned char* orow = xrow + (size_t)CH * 16 * BLOCK;     // OCH * OCB * BLOCK bytes
+    unsigned char* dummy = orow + (size_t)OCH * OCB * BLOCK;  // 16 bytes
     const int tid = threadIdx.x;
     const int n_units = C / 8;
-    const int nchunks = C / 8;          // 16-byte chunks of an fp16 row
 
-    int src[UPL][8];
+    int src[UPL][8], zb[UPL][8], uob[UPL];
     float inv[UPL][8];
-    int zb[UPL][8];
 #pragma unroll
     for (int u = 0; u < UPL; ++u) {
-        const int unit = tid + u * kBlock;
+        const int unit = tid + u * BLOCK;
+        const bool live = unit < n_units;
+        uob[u] = live ? UnitGeom<BITS>::out_byte(unit) : (int)(dummy - orow);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             src[u][e] = 0; inv[u][e] = 0.0f; zb[u][e] = 0;
-            if (unit < n_units) {
+            if (live) {
                 const int j = UnitGeom<BITS>::first(unit) + e * UnitGeom<BITS>::stride;
                 const int c = cluster_of_pos(ca, j);
                 src[u][e] = (R ? R[j] : j) * 2;
@@ -52,66 +58,65 @@ __global__ __launch_bounds__(kBlock) void kv_quant_pack_kernel(
         }
     }
 
-    u32x4 buf[CH];
-    auto load_row = [&](int64_t t) {
-        const u32x4* g = reinterpret_cast<const u32x4*>(kv + t * C);
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * kBlock;
-            if (c < nchunks) buf[i] = __builtin_nontemporal_load(g + c);
-        }
-    };
-
-    int64_t t = blockIdx.x;
-    if (t < T) load_row(t);
-    for (; t < T; t += gridDim.x) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * kBlock;
-            if (c < nchunks) reinterpret_cast<u32x4*>(xrow)[c] = buf[i];
-        }
+    u32x4 bufA[CH], bufB[CH];
+    auto process = [&](u32x4 (&buf)[CH], int64_t t) {
+        put_row_chunks<true, CH>(xrow, buf);
         __syncthreads();
-        if (t + gridDim.x < T) load_row(t + gridDim.x);
+        if (t + 2 * (int64_t)gridDim.x < T)
+            load_row_chunks<true, CH>(buf, kv + (t + 2 * (int64_t)gridDim.x) * C, in_bytes);
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
-            const int unit = tid + u * kBlock;
-            if (unit >= n_units) continue;
             int q[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float v = (float)*reinterpret_cast<const _Float16*>(xrow + src[u][e]);
                 q[e] = quant_code(v, inv[u][e], zb[u][e], QMAX);
             }
-            store_unit<BITS>(orow, unit, q);
+            store_unit_at<BITS>(orow + uob[u], q);
         }
         __syncthreads();
-        store_row(packed + t * row_bytes, orow, row_bytes);
+        store_row_chunks<OVEC16, OCH>(packed + t * row_bytes, row_bytes, orow);
+    };
+
+    const int64_t G = gridDim.x;
+    int64_t t = blockIdx.x;
+    if (t < T) load_row_chunks<true, CH>(bufA, kv + t * C, in_bytes);
+    if (t + G < T) load_row_chunks<true, CH>(bufB, kv + (t + G) * C, in_bytes);
+    for (; t < T; t += 2 * G) {
+        process(bufA, t);
+        if (t + G >= T) break;
+        process(bufB, t + G);
     }
 }
 
-template <int BITS, int UPL>
-__global__ __launch_bounds__(kBlock) void kv_dequant_kernel(
+template <int BITS, int UPL, bool VEC16>
+__global__ __launch_bounds__(kMaxBlock) void kv_dequant_kernel(
     const uint8_t* __restrict__ packed, int64_t T, int32_t C, const int32_t* __restrict__ R,
     const ClusterArgs ca, uint16_t* __restrict__ out) {
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int CH = (kMaxK * BITS / 8 / 4 + kBlock - 1) / kBlock;   // 4-byte chunks per thread
+    constexpr int CB = VEC16 ? 16 : 4;
+    constexpr int CH = chunks_for<VEC16>(UPL * BITS);         // packed row: C*BITS/8 bytes
+    constexpr int OCH = UPL;                                  // fp16 row: C/8 chunks
+    const int BLOCK = blockDim.x;
     const int64_t row_bytes = (int64_t)C * BITS / 8;
-    unsigned char* prow = smem;                                    // packed row
-    unsigned char* orow = smem + align16(row_bytes);               // fp16 row, natural order
+    const int64_t out_bytes = (int64_t)C * 2;
+    unsigned char* prow = smem;                               // CH * CB * BLOCK bytes
+    unsigned char* orow = prow + (size_t)CH * CB * BLOCK;     // OCH * 16 * BLOCK bytes
+    unsigned char* dummy = orow + (size_t)OCH * 16 * BLOCK;   // 16 bytes
     const int tid = threadIdx.x;
     const int n_units = C / 8;
-    const int nwords = (int)(row_bytes / 4);
 
-    int dst[UPL][8];
-    float sc[UPL][8];
-    float zf[UPL][8];
+    int dst[UPL][8], uib[UPL];
+    float sc[UPL][8], zf[UPL][8];
 #pragma unroll
     for (int u = 0; u < UPL; ++u) {
-        const int unit = tid + u * kBlock;
+        const int unit = tid + u * BLOCK;
+        const bool live = unit < n_units;
+        uib[u] = live ? UnitGeom<BITS>::out_byte(unit) : 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            dst[u][e] = 0; sc[u][e] = 0.0f; zf[u][e] = 0.0f;
-            if (unit < n_units) {
+            dst[u][e] = (int)(dummy - orow); sc[u][e] = 0.0f; zf[u][e] = 0.0f;
+            if (live) {
                 const int j = UnitGeom<BITS>::first(unit) + e * UnitGeom<BITS>::stride;
                 const int c = cluster_of_pos(ca, j);
                 dst[u][e] = (R ? R[j] : j) * 2;
@@ -121,32 +126,16 @@ __global__ __launch_bounds__(kBlock) void kv_dequant_kernel(
         }
     }
 
-    uint32_t buf[CH];
-    auto load_row = [&](int64_t t) {
-        const uint32_t* g = reinterpret_cast<const uint32_t*>(packed + t * row_bytes);
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * kBlock;
-            if (c < nwords) buf[i] = __builtin_nontemporal_load(g + c);
-        }
-    };
-
-    int64_t t = blockIdx.x;
-    if (t < T) load_row(t);
-    for (; t < T; t += gridDim.x) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * kBlock;
-            if (c < nwords) reinterpret_cast<uint32_t*>(prow)[c] = buf[i];
-        }
+    chunk_t<VEC16> bufA[CH], bufB[CH];
+    auto process = [&](chunk_t<VEC16> (&buf)[CH], int64_t t) {
+        put_row_chunks<VEC16, CH>(prow, buf);
         __syncthreads();
-        if (t + gridDim.x < T) load_row(t + gridDim.x);
+        if (t + 2 * (int64_t)gridDim.x < T)
+            load_row_chunks<VEC16, CH>(buf, packed + (t + 2 * (int64_t)gridDim.x) * row_bytes, row_bytes);
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
-            const int unit = tid + u * kBlock;
-            if (unit >= n_units) continue;
             int q[8];
-            load_unit<BITS>(prow, unit, q);
+            load_unit_at<BITS>(prow + uib[u], q);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 // (q - z) is an exact integer in fp32; the product is rounded
@@ -156,62 +145,98 @@ __global__ __launch_bounds__(kBlock) void kv_dequant_kernel(
             }
         }
         __syncthreads();
-        store_row(reinterpret_cast<uint8_t*>(out + t * C), orow, (int64_t)C * 2);
+        store_row_chunks<true, OCH>(out + t * C, out_bytes, orow);
+    };
+
+    const int64_t G = gridDim.x;
+    int64_t t = blockIdx.x;
+    if (t < T) load_row_chunks<VEC16, CH>(bufA, packed + t * row_bytes, row_bytes);
+    if (t + G < T) load_row_chunks<VEC16, CH>(bufB, packed + (t + G) * row_bytes, row_bytes);
+    for (; t < T; t += 2 * G) {
+        process(bufA, t);
+        if (t + G >= T) break;
+        process(bufB, t + G);
     }
 }
 
-template <int BITS>
-const void* pick_quant(int upl) {
+template <int BITS, bool V>
+const void* pick_quant_v(int upl) {
     switch (upl) {
-        case 1: return (const void*)kv_quant_pack_kernel<BITS, 1>;
-        case 2: return (const void*)kv_quant_pack_kernel<BITS, 2>;
-        case 3: return (const void*)kv_quant_pack_kernel<BITS, 3>;
-        case 4: return (const void*)kv_quant_pack_kernel<BITS, 4>;
-        case 5: return (const void*)kv_quant_pack_kernel<BITS, 5>;
-        case 6: return (const void*)kv_quant_pack_kernel<BITS, 6>;
-        case 7: return (const void*)kv_quant_pack_kernel<BITS, 7>;
-        case 8: return (const void*)kv_quant_pack_kernel<BITS, 8>;
+        case 1: return (const void*)kv_quant_pack_kernel<BITS, 1, V>;
+        case 2: return (const void*)kv_quant_pack_kernel<BITS, 2, V>;
+        case 3: return (const void*)kv_quant_pack_kernel<BITS, 3, V>;
+        case 4: return (const void*)kv_quant_pack_kernel<BITS, 4, V>;
+        case 5: return (const void*)kv_quant_pack_kernel<BITS, 5, V>;
         default: return nullptr;
     }
 }
 
-template <int BITS>
-const void* pick_dequant(int upl) {
+template <int BITS, bool V>
+const void* pick_dequant_v(int upl) {
     switch (upl) {
-        case 1: return (const void*)kv_dequant_kernel<BITS, 1>;
-        case 2: return (const void*)kv_dequant_kernel<BITS, 2>;
-        case 3: return (const void*)kv_dequant_kernel<BITS, 3>;
-        case 4: return (const void*)kv_dequant_kernel<BITS, 4>;
-        case 5: return (const void*)kv_dequant_kernel<BITS, 5>;
-        case 6: return (const void*)kv_dequant_kernel<BITS, 6>;
-        case 7: return (const void*)kv_dequant_kernel<BITS, 7>;
-        case 8: return (const void*)kv_dequant_kernel<BITS, 8>;
+        case 1: return (const void*)kv_dequant_kernel<BITS, 1, V>;
+        case 2: return (const void*)kv_dequant_kernel<BITS, 2, V>;
+        case 3: return (const void*)kv_dequant_kernel<BITS, 3, V>;
+        case 4: return (const void*)kv_dequant_kernel<BITS, 4, V>;
+        case 5: return (const void*)kv_dequant_kernel<BITS, 5, V>;
         default: return nullptr;
     }
+}
+
+template <bool QUANT>
+const void* pick(int bits, int upl, bool v16) {
+    if (QUANT) {
+        if (bits == 3) return v16 ? pick_quant_v<3, true>(upl) : pick_quant_v<3, false>(upl);
+        if (bits == 4) return v16 ? pick_quant_v<4, true>(upl) : pick_quant_v<4, false>(upl);
+        return v16 ? pick_quant_v<8, true>(upl) : pick_quant_v<8, false>(upl);
+    }
+    if (bits == 3) return v16 ? pick_dequant_v<3, true>(upl) : pick_dequant_v<3, false>(upl);
+    if (bits == 4) return v16 ? pick_dequant_v<4, true>(upl) : pick_dequant_v<4, false>(upl);
+    return v16 ? pick_dequant_v<8, true>(upl) : pick_dequant_v<8, false>(upl);
+}
+
+// LDS bytes: the fp16 row and the packed row, each rounded up to whole lanes
+// x chunks, plus the 16-byte dummy slot.
+size_t kv_lds(int bits, int upl, int block, bool v16) {
+    const int cb = v16 ? 16 : 4;
+    const int pch = v16 ? (upl * bits + 15) / 16 : (upl * bits + 3) / 4;
+    return (size_t)upl * 16 * block + (size_t)pch * cb * block + 16;
 }
 
 }  // namespace
 
 hipError_t launch_kv_quant_pack(const uint16_t* kv, int64_t T, int32_t C, const int32_t* R,
                                 const ClusterArgs& ca, uint8_t* packed, hipStream_t stream) {
-    const int upl = (C / 8 + kBlock - 1) / kBlock;
-    const void* k = ca.bits == 3 ? pick_quant<3>(upl) : ca.bits == 4 ? pick_quant<4>(upl) : pick_quant<8>(upl);
+    int upl = 0, block = 0;
+    unit_split(C / 8, upl, block);
+    const bool v16 = ((int64_t)C * ca.bits / 8) % 16 == 0;
+    const void* k = pick<true>(ca.bits, upl, v16);
     if (!k) return hipErrorInvalidValue;
-    const size_t lds = (size_t)align16((int64_t)C * 2) + align16((int64_t)C * ca.bits / 8);
-    const int grid = persistent_grid(k, kBlock, lds, T);
+    const size_t lds = kv_lds(ca.bits, upl, block, v16);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const int grid = persistent_grid(k, block, lds, T);
     void* args[] = {(void*)&kv, (void*)&T, (void*)&C, (void*)&R, (void*)&ca, (void*)&packed};
-    return hipLaunchKernel(k, dim3(grid), dim3(kBlock), args, lds, stream);
+    return hipLaunchKernel(k, dim3(grid), dim3(block), args, lds, stream);
 }
 
 hipError_t launch_kv_dequant(const uint8_t* packed, int64_t T, int32_t C, const int32_t* R,
                              const ClusterArgs& ca, uint16_t* out, hipStream_t stream) {
-    const int upl = (C / 8 + kBlock - 1) / kBlock;
-    const void* k = ca.bits == 3 ? pick_dequant<3>(upl) : ca.bits == 4 ? pick_dequant<4>(upl) : pick_dequant<8>(upl);
+    int upl = 0, block = 0;
+    unit_split(C / 8, upl, block);
+    const bool v16 = ((int64_t)C * ca.bits / 8) % 16 == 0;
+    const void* k = pick<false>(ca.bits, upl, v16);
     if (!k) return hipErrorInvalidValue;
-    const size_t lds = (size_t)align16((int64_t)C * ca.bits / 8) + align16((int64_t)C * 2);
-    const int grid = persistent_grid(k, kBlock, lds, T);
+    const size_t lds = kv_lds(ca.bits, upl, block, v16);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const int grid = persistent_grid(k, block, lds, T);
     void* args[] = {(void*)&packed, (void*)&T, (void*)&C, (void*)&R, (void*)&ca, (void*)&out};
-    return hipLaunchKernel(k, dim3(grid), dim3(kBlock), args, lds, stream);
+    return hipLaunchKernel(k, dim3(grid), dim3(block), args, lds, stream);
 }
 
 }  // namespace rptq

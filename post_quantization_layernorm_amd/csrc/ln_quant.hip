@@ -5,40 +5,57 @@
 // buffer; each cluster of reordered channels has its own (s, z).  The kernel
 // is HBM-bound: it reads fp16 [M][K] once and writes b-bit codes once.
 //
-// Design (one persistent workgroup of 256 or 512 threads per row at a time):
-//   - every lane owns a fixed set of "units" (8 output codes each) for all
-//     rows; the source channel R[j], gamma'[j], beta'[j] and the cluster's
-//     (1/s, z) of its units stay in registers across rows;
-//   - a row is read with 16-byte coalesced loads (the next row's loads are in
-//     flight while the current row is quantized), the mean and the biased
-//     variance are two wave-shuffle reductions over the register copy
-//     (two-pass, fp32), and the row is parked in LDS in natural order;
-//   - each unit gathers its 8 inputs from LDS by R, normalizes, quantizes and
-//     packs them into an LDS copy of the output row, which is then written
-//     with 16-byte coalesced stores.
+// Design (persistent workgroups, one row at a time per workgroup):
+//   - the workgroup size (a multiple of 64) is chosen so that each lane owns
+//     few "units" (8 output codes each); a lane keeps, for all rows, the
+//     source channel R[j], gamma'[j], beta'[j] of its units and the cluster's
+//     (1/s, z) in registers;
+//   - rows are read with 16-byte buffer loads into two register buffers, so
+//     two rows per workgroup are in flight while one is quantized.  Every
+//     memory instruction runs unconditionally (lanes past the row end read
+//     zeros / have their stores dropped by the buffer range check), which
+//     keeps the compiler's memory-counter waits exact: a row's wait never
+//     covers the next row's loads;
+//   - mean and biased variance come from packed-fp16 dot products
+//     (sum x and sum x^2 in fp32, one VALU op per element) and one
+//     wave-shuffle + LDS reduction; if more than 6 bits would cancel in
+//     E[x^2] - E[x]^2, an exact second pass around the mean is taken;
+//   - the row is parked in LDS in natural order; each unit gathers its 8
+//     inputs by R, normalizes, quantizes and packs them into an LDS copy of
+//     the output row, which is written with 16-byte stores.
 #include "rptq_device.hpp"
 #include "../../include/rptq.h"
 
 namespace rptq {
 namespace {
 
-__host__ __device__ constexpr int align16(int64_t b) { return (int)((b + 15) & ~int64_t(15)); }
-
-template <int BLOCK>
 __device__ __forceinline__ float block_sum(float v, float* scratch) {
     v = wave_sum(v);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
     if (lane == 0) scratch[w] = v;
     __syncthreads();
     float t = 0.0f;
-#pragma unroll
-    for (int i = 0; i < BLOCK / 64; ++i) t += scratch[i];
+    for (int i = 0; i < nw; ++i) t += scratch[i];
     __syncthreads();
     return t;
 }
 
-template <int BITS, int MODE, int UPL, int BLOCK>
-__global__ __launch_bounds__(BLOCK) void ln_reorder_quant_kernel(
+// Two sums over the workgroup in one exchange (one pair of barriers).
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* scratch) {
+    a = wave_sum(a);
+    b = wave_sum(b);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if (lane == 0) { scratch[2 * w] = a; scratch[2 * w + 1] = b; }
+    __syncthreads();
+    float ta = 0.0f, tb = 0.0f;
+    for (int i = 0; i < nw; ++i) { ta += scratch[2 * i]; tb += scratch[2 * i + 1]; }
+    __syncthreads();
+    a = ta;
+    b = tb;
+}
+
+template <int BITS, int MODE, int UPL>
+__global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
     const void* __restrict__ xin, int64_t M, int32_t K, int64_t row_bytes,
     const float* __restrict__ gamma_r, const float* __restrict__ beta_r, float eps,
     const int32_t* __restrict__ R, const ClusterArgs ca, uint8_t* __restrict__ codes) {
@@ -46,26 +63,36 @@ __global__ __launch_bounds__(BLOCK) void ln_reorder_quant_kernel(
     constexpr int QMAX = (1 << BITS) - 1;
     constexpr bool LN = MODE == RPTQ_IN_FP16_RAW;
     constexpr int ESZ = LN ? 2 : 4;                       // bytes per input element
-    constexpr int CH = (kMaxK * ESZ / 16 + BLOCK - 1) / BLOCK;   // 16-B chunks per thread
+    // 16-byte input chunks per lane: a row has K*ESZ/16 chunks and at least
+    // K/8 units, so ESZ/2 * UPL chunks per lane always suffice
+    constexpr int CH = UPL * ESZ / 2;
+    // 16-byte output chunks per lane: a packed row has at most units*BITS bytes
+    constexpr int OCH = (UPL * BITS + 15) / 16;
+    const int BLOCK = blockDim.x;
     const int row_in_bytes = K * ESZ;
+    // LDS: input row (rounded up to whole lanes x chunks), output row, a
+    // dummy slot for idle units, reduction scratch
     unsigned char* xrow = smem;
-    unsigned char* orow = smem + align16(row_in_bytes);
-    float* red = reinterpret_cast<float*>(orow + align16(row_bytes));
+    unsigned char* orow = smem + (size_t)CH * 16 * BLOCK;
+    unsigned char* dummy = orow + (size_t)OCH * 16 * BLOCK;
+    float* red = reinterpret_cast<float*>(dummy + 16);
     const int tid = threadIdx.x;
     const int n_units = ca.K_pad / 8;
     const int nchunks = row_in_bytes / 16;
 
-    // ---- per-lane unit tables (fixed for every row)
+    // ---- per-lane unit tables (fixed for every row); idle units gather
+    // element 0 and write to the dummy slot
     int src[UPL][8];
     float gam[UPL][8], bet[UPL][8];
     float uinv[UPL];
-    int uzb[UPL], unv[UPL];
+    int uzb[UPL], unv[UPL], uob[UPL];
 #pragma unroll
     for (int u = 0; u < UPL; ++u) {
         const int unit = tid + u * BLOCK;
-        unv[u] = -1;
+        unv[u] = 0;
         uinv[u] = 0.0f;
         uzb[u] = 0;
+        uob[u] = (int)(dummy - orow);
 #pragma unroll
         for (int e = 0; e < 8; ++e) { src[u][e] = 0; gam[u][e] = 0.0f; bet[u][e] = 0.0f; }
         if (unit < n_units) {
@@ -74,6 +101,7 @@ __global__ __launch_bounds__(BLOCK) void ln_reorder_quant_kernel(
             const int n_c = ca.bounds[c + 1] - ca.bounds[c];
             uinv[u] = ca.inv_s[c];
             uzb[u] = ca.z[c] - kRoundMagicBits;
+            uob[u] = UnitGeom<BITS>::out_byte(unit);
             int nv = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -94,65 +122,68 @@ __global__ __launch_bounds__(BLOCK) void ln_reorder_quant_kernel(
         }
     }
 
-    u32x4 buf[CH];
-    auto load_row = [&](int64_t row) {
-        const u32x4* g = reinterpret_cast<const u32x4*>(static_cast<const char*>(xin) + row * row_in_bytes);
+    // Two register buffers: while row r (in one) is processed, row r + G is
+    // in flight in the other (G = gridDim.x).
+    u32x4 bufA[CH], bufB[CH];
+    auto load_row = [&](u32x4 (&buf)[CH], int64_t row) {
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(static_cast<const uint8_t*>(xin) + row * row_in_bytes, row_in_bytes);
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * BLOCK;
-            if (c < nchunks) buf[i] = __builtin_nontemporal_load(g + c);
-        }
+        for (int i = 0; i < CH; ++i)
+            buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(tid + i * BLOCK) * 16u, 0, 0);
     };
 
-    int64_t row = blockIdx.x;
-    if (row < M) load_row(row);
-    for (; row < M; row += gridDim.x) {
+    auto process = [&](u32x4 (&buf)[CH], int64_t row) {
         float mean = 0.0f, rstd = 0.0f;
         if constexpr (LN) {
-            // pass 1: sum (packed fp16 dot products against 1.0, fp32 accumulate)
+            // sum x and sum x^2 from packed fp16 dot products (exact
+            // products, fp32 accumulation); chunks past the row are zeros
             const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
-            float s = 0.0f;
+            float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
-                if (tid + i * BLOCK < nchunks) {
-                    const uint32_t w[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
+                const uint32_t w[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
 #pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[k]), one2, s, false);
+                for (int k = 0; k < 4; ++k) {
+                    const half2_t h = __builtin_bit_cast(half2_t, w[k]);
+                    s1 = __builtin_amdgcn_fdot2(h, one2, s1, false);
+                    s2 = __builtin_amdgcn_fdot2(h, h, s2, false);
                 }
             }
-            s = block_sum<BLOCK>(s, red);
-            mean = s / (float)K;
-            // pass 2: biased variance around the mean
-            float ss = 0.0f;
+            block_sum2(s1, s2, red);
+            const float m1 = s1 / (float)K, m2 = s2 / (float)K;
+            float var = m2 - m1 * m1;
+            mean = m1;
+            if (!(var > m2 * 0.015625f)) {
+                // more than 6 bits would cancel (|mean| >> spread, or a
+                // constant row): exact second pass around the mean
+                float ss = 0.0f;
 #pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                if (tid + i * BLOCK < nchunks) {
-                    const uint32_t w[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
+                for (int i = 0; i < CH; ++i) {
+                    if (tid + i * BLOCK < nchunks) {
+                        const uint32_t w[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const half2_t h = __builtin_bit_cast(half2_t, w[k]);
-                        const float d0 = (float)h.x - mean, d1 = (float)h.y - mean;
-                        ss = __builtin_fmaf(d0, d0, ss);
-                        ss = __builtin_fmaf(d1, d1, ss);
+                        for (int k = 0; k < 4; ++k) {
+                            const half2_t h = __builtin_bit_cast(half2_t, w[k]);
+                            const float d0 = (float)h.x - mean, d1 = (float)h.y - mean;
+                            ss = __builtin_fmaf(d0, d0, ss);
+                            ss = __builtin_fmaf(d1, d1, ss);
+                        }
                     }
                 }
+                ss = block_sum(ss, red);
+                var = ss / (float)K;
             }
-            ss = block_sum<BLOCK>(ss, red);
-            rstd = 1.0f / __builtin_sqrtf(ss / (float)K + eps);
+            rstd = 1.0f / __builtin_sqrtf(var + eps);
         }
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * BLOCK;
-            if (c < nchunks) reinterpret_cast<u32x4*>(xrow)[c] = buf[i];
-        }
+        for (int i = 0; i < CH; ++i) reinterpret_cast<u32x4*>(xrow)[tid + i * BLOCK] = buf[i];
         __syncthreads();
-        if (row + gridDim.x < M) load_row(row + gridDim.x);      // next row in flight
+        if (row + 2 * (int64_t)gridDim.x < M) load_row(buf, row + 2 * (int64_t)gridDim.x);
 
         const float nmr = -mean * rstd;
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
-            if (unv[u] < 0) continue;
             int q[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -167,28 +198,34 @@ __global__ __launch_bounds__(BLOCK) void ln_reorder_quant_kernel(
                 const int qq = quant_code(y, uinv[u], uzb[u], QMAX);
                 q[e] = e < unv[u] ? qq : 0;
             }
-            store_unit<BITS>(orow, tid + u * BLOCK, q);
+            store_unit_at<BITS>(orow + uob[u], q);
         }
         __syncthreads();
-        store_row(codes + row * row_bytes, orow, row_bytes);
-    }
-}
+        // 3-bit rows are a multiple of 12 bytes: 4-byte stores
+        store_row_chunks<BITS != 3, chunks_for<BITS != 3>(UPL * BITS)>(codes + row * row_bytes, row_bytes, orow);
+    };
 
-template <int BITS, int MODE, int BLOCK>
-const void* pick_kernel(int upl) {
-    switch (upl) {
-        case 1: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 1, BLOCK>;
-        case 2: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 2, BLOCK>;
-        case 3: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 3, BLOCK>;
-        case 4: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 4, BLOCK>;
-        case 5: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 5, BLOCK>;
-        default: return nullptr;
+    const int64_t G = gridDim.x;
+    int64_t row = blockIdx.x;
+    if (row < M) load_row(bufA, row);
+    if (row + G < M) load_row(bufB, row + G);
+    for (; row < M; row += 2 * G) {
+        process(bufA, row);
+        if (row + G >= M) break;
+        process(bufB, row + G);
     }
 }
 
 template <int BITS, int MODE>
-const void* pick(int upl, int block) {
-    return block == 256 ? pick_kernel<BITS, MODE, 256>(upl) : pick_kernel<BITS, MODE, 512>(upl);
+const void* pick(int upl) {
+    switch (upl) {
+        case 1: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 1>;
+        case 2: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 2>;
+        case 3: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 3>;
+        case 4: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 4>;
+        case 5: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 5>;
+        default: return nullptr;
+    }
 }
 
 }  // namespace
@@ -197,18 +234,18 @@ hipError_t launch_ln_reorder_quant(const void* x, int in_mode, int64_t M, int32_
                                    const float* gamma_r, const float* beta_r, float eps,
                                    const int32_t* R, const ClusterArgs& ca, int64_t row_bytes,
                                    uint8_t* codes, hipStream_t stream) {
-    const int n_units = ca.K_pad / 8;
-    const int block = n_units <= 5 * 256 ? 256 : 512;
-    const int upl = (n_units + block - 1) / block;
+    int upl = 0, block = 0;
+    unit_split(ca.K_pad / 8, upl, block, RPTQ_LN_MAX_BLOCK);
     const void* k = nullptr;
     if (in_mode == RPTQ_IN_FP16_RAW) {
-        k = ca.bits == 3 ? pick<3, 0>(upl, block) : ca.bits == 4 ? pick<4, 0>(upl, block) : pick<8, 0>(upl, block);
+        k = ca.bits == 3 ? pick<3, 0>(upl) : ca.bits == 4 ? pick<4, 0>(upl) : pick<8, 0>(upl);
     } else {
-        k = ca.bits == 3 ? pick<3, 1>(upl, block) : ca.bits == 4 ? pick<4, 1>(upl, block) : pick<8, 1>(upl, block);
+        k = ca.bits == 3 ? pick<3, 1>(upl) : ca.bits == 4 ? pick<4, 1>(upl) : pick<8, 1>(upl);
     }
     if (!k) return hipErrorInvalidValue;
     const int esz = in_mode == RPTQ_IN_FP16_RAW ? 2 : 4;
-    const size_t lds = (size_t)align16((int64_t)K * esz) + align16(row_bytes) + 64;
+    const int ch = upl * esz / 2, och = (upl * ca.bits + 15) / 16;
+    const size_t lds = (size_t)ch * 16 * block + (size_t)och * 16 * block + 16 + 128;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;

@@ -46,12 +46,6 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 constexpr int GROUP_M = 8;
-constexpr uint32_t kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
-    const int32_t n = bytes <= 0 ? 0 : bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, kRsrcWord3);
-}
 
 // One 32-code piece of BITS-bit codes = BITS 32-bit words.
 template <int BITS>

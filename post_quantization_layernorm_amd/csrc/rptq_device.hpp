@@ -2,6 +2,7 @@
 #pragma once
 
 #include <cstdint>
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -11,6 +12,14 @@ namespace rptq {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): loads past the end read as
+// zero and stores past the end are dropped (range check in hardware).
+constexpr uint32_t kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int32_t n = bytes <= 0 ? 0 : bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
+}
 
 // Code of one value v with a cluster's fp32 reciprocal scale inv_s and
 // zb = z - kRoundMagicBits:
@@ -46,6 +55,8 @@ __device__ __forceinline__ float block_sum_256(float v, float* scratch) {
     return t;
 }
 
+constexpr int kCalibBlock = 256;
+
 // Positions of the 8 codes a "unit" covers, in a row laid out in groups (see
 // rptq.h).  For 4- and 8-bit rows a unit is 8 consecutive codes; for 3-bit
 // rows a unit is byte lane `bl` of a 32-code group: codes bl, bl+4, ..., bl+28.
@@ -62,32 +73,85 @@ struct UnitGeom {
 };
 
 // Pack the 8 codes of a unit (q[e] is the code at position first + e*stride)
-// and store them into the packed row `out` (LDS) at the unit's byte offset.
+// and store them at p, the unit's first output byte in a packed row (LDS).
 template <int BITS>
-__device__ __forceinline__ void store_unit(unsigned char* out, int unit, const int (&q)[8]) {
-    const int ob = UnitGeom<BITS>::out_byte(unit);
+__device__ __forceinline__ void store_unit_at(unsigned char* p, const int (&q)[8]) {
     if constexpr (BITS == 8) {
         uint2 v;
         v.x = (uint32_t)q[0] | (uint32_t)q[1] << 8 | (uint32_t)q[2] << 16 | (uint32_t)q[3] << 24;
         v.y = (uint32_t)q[4] | (uint32_t)q[5] << 8 | (uint32_t)q[6] << 16 | (uint32_t)q[7] << 24;
-        *reinterpret_cast<uint2*>(out + ob) = v;
+        *reinterpret_cast<uint2*>(p) = v;
     } else if constexpr (BITS == 4) {
         uint32_t v = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v |= ((uint32_t)q[i] | (uint32_t)q[4 + i] << 4) << (8 * i);
-        *reinterpret_cast<uint32_t*>(out + ob) = v;
+        *reinterpret_cast<uint32_t*>(p) = v;
     } else {
-        // byte lane bl of words d0, d1, d2 of the group
-        out[ob] = (unsigned char)(q[0] | q[1] << 3 | (q[6] & 3) << 6);
-        out[ob + 4] = (unsigned char)(q[2] | q[3] << 3 | (q[7] & 3) << 6);
-        out[ob + 8] = (unsigned char)(q[4] | q[5] << 3 | (q[6] >> 2) << 6 | (q[7] >> 2) << 7);
+        // byte lane of words d0, d1, d2 of the 32-code group
+        p[0] = (unsigned char)(q[0] | q[1] << 3 | (q[6] & 3) << 6);
+        p[4] = (unsigned char)(q[2] | q[3] << 3 | (q[7] & 3) << 6);
+        p[8] = (unsigned char)(q[4] | q[5] << 3 | (q[6] >> 2) << 6 | (q[7] >> 2) << 7);
     }
 }
 
-// Inverse of store_unit: the 8 codes of a unit from a packed row (LDS).
 template <int BITS>
-__device__ __forceinline__ void load_unit(const unsigned char* in, int unit, int (&q)[8]) {
-    const int ob = UnitGeom<BITS>::out_byte(unit);
+__device__ __forceinline__ void store_unit(unsigned char* out, int unit, const int (&q)[8]) {
+    store_unit_at<BITS>(out + UnitGeom<BITS>::out_byte(unit), q);
+}
+
+// Row transfers with buffer instructions that every lane executes (accesses
+// past `bytes` read zeros / are dropped by the buffer range check), so the
+// compiler's memory-counter waits stay exact.  Chunk i of lane t is chunk
+// t + i * blockDim.x of the row; chunks are 16 bytes (VEC16) or 4 bytes, and
+// `bytes` must be a multiple of the chunk size.
+template <bool VEC16>
+using chunk_t = typename std::conditional<VEC16, u32x4, uint32_t>::type;
+
+template <bool VEC16, int N>
+__device__ __forceinline__ void load_row_chunks(chunk_t<VEC16> (&buf)[N], const void* base, int64_t bytes) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, bytes);
+    const int tid = threadIdx.x, nt = blockDim.x;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if constexpr (VEC16)
+            buf[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(tid + i * nt) * 16u, 0, 0);
+        else
+            buf[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(tid + i * nt) * 4u, 0, 0);
+    }
+}
+
+template <bool VEC16, int N>
+__device__ __forceinline__ void put_row_chunks(unsigned char* lds, const chunk_t<VEC16> (&buf)[N]) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+#pragma unroll
+    for (int i = 0; i < N; ++i) reinterpret_cast<chunk_t<VEC16>*>(lds)[tid + i * nt] = buf[i];
+}
+
+template <bool VEC16, int N>
+__device__ __forceinline__ void store_row_chunks(void* base, int64_t bytes, const unsigned char* lds) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, bytes);
+    const int tid = threadIdx.x, nt = blockDim.x;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int c = tid + i * nt;
+        if constexpr (VEC16)
+            __builtin_amdgcn_raw_buffer_store_b128(reinterpret_cast<const u32x4*>(lds)[c], r, (uint32_t)c * 16u, 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(reinterpret_cast<const uint32_t*>(lds)[c], r, (uint32_t)c * 4u, 0, 0);
+    }
+}
+
+// Chunks per lane that cover `bytes_per_lane` bytes.
+template <bool VEC16>
+__host__ __device__ constexpr int chunks_for(int bytes_per_lane) {
+    return VEC16 ? (bytes_per_lane + 15) / 16 : (bytes_per_lane + 3) / 4;
+}
+
+// Inverse of store_unit_at: the 8 codes of a unit whose first byte is at p.
+template <int BITS>
+__device__ __forceinline__ void load_unit_at(const unsigned char* p, int (&q)[8]) {
+    const unsigned char* in = p;
+    constexpr int ob = 0;
     if constexpr (BITS == 8) {
         const uint2 v = *reinterpret_cast<const uint2*>(in + ob);
 #pragma unroll

@@ -9,7 +9,25 @@ namespace rptq {
 
 constexpr int kMaxClusters = 64;
 constexpr int kMaxK = 16384;
-constexpr int kBlock = 256;            // threads per workgroup of the streaming kernels
+constexpr int kMaxBlock = 512;         // largest workgroup of the streaming kernels
+constexpr int kMaxUpl = 5;             // most units (8 codes each) one lane handles
+#ifndef RPTQ_LN_MAX_BLOCK
+#define RPTQ_LN_MAX_BLOCK 256          // LayerNorm kernel: fewer, fatter lanes (two workgroups per CU)
+#endif
+
+// Workgroup size and units per lane for a row of n_units units: the smallest
+// units-per-lane whose workgroup (rounded up to whole waves) fits pref_block,
+// else fits kMaxBlock; upl = 0 if the row is too long for either.
+inline void unit_split(int n_units, int& upl, int& block, int pref_block = kMaxBlock) {
+    for (int cap : {pref_block, kMaxBlock}) {
+        for (upl = 1; upl <= kMaxUpl; ++upl) {
+            block = ((n_units + upl - 1) / upl + 63) / 64 * 64;
+            if (block <= cap) return;
+        }
+    }
+    upl = 0;
+    block = 0;
+}
 
 // Cluster table, passed by value as a kernel argument (about 1.6 KB, well
 // under the kernel-argument limit).  Built and validated on the host.
