@@ -12,7 +12,17 @@ Inputs are generated (seeded, synthetic) and resident in HBM before the timed
 region.  `value` is the tokens/s of the W4A4 LayerNorm-quant -> GEMM pair,
 tokens / (t_LN + t_GEMM), with kernel times from HIP events recorded on the
 stream the kernels are launched on; the other kernels' rates are extra keys.
-`--gpus N` with N > 1 is refused: this build measures one GPU.
+`--gpus N` with N > 1 is refused: the library drives one GPU per process and
+has no multi-GPU path.
+
+Profiling helpers (not part of the timed step):
+  --copy-probe       after the timed region, one plain device copy of
+                     COPY_PROBE_BYTES, whose counter readings calibrate the HBM
+                     byte counters;
+  --ingest-pmc F W   read two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then
+                     WRITE_SIZE), scale them by the copy probe and write the
+                     per-launch HBM traffic of each kernel to
+                     profiles/hbm_traffic.json.
 """
 from __future__ import annotations
 
@@ -72,10 +82,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline leg (0: leave it out)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed region, run one plain device copy of COPY_PROBE_BYTES")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: every box in this setup has a single MI355X and the "
-              "library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(rows shard across GPUs without any exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -123,23 +140,22 @@ def main():
     kvw = synthetic.KV_WORKLOADS["opt66b_kv_a3"]
     T, C, kvb = kvw.T, kvw.C, kvw.bits
     kv = {}
-    if True:
-        for name, (s_ch, s_cal, s_ev) in {"K": (synthetic.STREAM_CHANNELS, synthetic.STREAM_CALIB,
-                                                synthetic.STREAM_EVAL),
-                                          "V": (synthetic.STREAM_CHANNELS_V, synthetic.STREAM_CALIB_V,
-                                                synthetic.STREAM_EVAL_V)}.items():
-            kmu, ksg = synthetic.channel_params(C, kvw.seed, kvw.outlier_frac, stream=s_ch)
-            kc = torch.from_numpy(synthetic.tokens(kvw.calib_tokens, kmu, ksg, kvw.seed, s_cal)).to(dev)
-            kmx, kmn = P.rptq_calib_minmax(kc, P.RPTQ_CALIB_RAW)
-            kmx, kmn = kmx.cpu().numpy(), kmn.cpu().numpy()
-            kR, kbnd = P.rptq_kmeans_reorder(kmx, kmn, kvw.g, synthetic.kmeans_uniforms(kvw.seed + len(name), 10,
-                                                                                      kvw.g), n_init=10)
-            ks, kz = P.rptq_cluster_params(kmx, kmn, kR, kbnd, kvb)
-            data = synthetic.tokens_device(T, kmu, ksg, kvw.seed, s_ev)
-            kv[name] = dict(x=data, R=torch.from_numpy(kR).to(dev), bounds=kbnd, s=ks, z=kz,
-                            packed=torch.empty((T, P.rptq_kv_row_bytes(C, kvb)), dtype=torch.uint8, device=dev),
-                            out=torch.empty((T, C), dtype=torch.float16, device=dev))
-        log(f"[bench] KV caches ready ({time.time() - t_setup:.1f}s)")
+    for name, (s_ch, s_cal, s_ev) in {"K": (synthetic.STREAM_CHANNELS, synthetic.STREAM_CALIB,
+                                            synthetic.STREAM_EVAL),
+                                      "V": (synthetic.STREAM_CHANNELS_V, synthetic.STREAM_CALIB_V,
+                                            synthetic.STREAM_EVAL_V)}.items():
+        kmu, ksg = synthetic.channel_params(C, kvw.seed, kvw.outlier_frac, stream=s_ch)
+        kc = torch.from_numpy(synthetic.tokens(kvw.calib_tokens, kmu, ksg, kvw.seed, s_cal)).to(dev)
+        kmx, kmn = P.rptq_calib_minmax(kc, P.RPTQ_CALIB_RAW)
+        kmx, kmn = kmx.cpu().numpy(), kmn.cpu().numpy()
+        kR, kbnd = P.rptq_kmeans_reorder(kmx, kmn, kvw.g, synthetic.kmeans_uniforms(kvw.seed + len(name), 10,
+                                                                                  kvw.g), n_init=10)
+        ks, kz = P.rptq_cluster_params(kmx, kmn, kR, kbnd, kvb)
+        data = synthetic.tokens_device(T, kmu, ksg, kvw.seed, s_ev)
+        kv[name] = dict(x=data, R=torch.from_numpy(kR).to(dev), bounds=kbnd, s=ks, z=kz,
+                        packed=torch.empty((T, P.rptq_kv_row_bytes(C, kvb)), dtype=torch.uint8, device=dev),
+                        out=torch.empty((T, C), dtype=torch.float16, device=dev))
+    log(f"[bench] KV caches ready ({time.time() - t_setup:.1f}s)")
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ one step
@@ -159,18 +175,17 @@ def main():
                          stream=stream)
             k += 2
         rec(k)
-        if True:
-            for name in ("K", "V"):
-                d = kv[name]
-                P.rptq_kv_quant_pack(d["x"], d["R"], d["bounds"], d["s"], d["z"], kvb, out=d["packed"], stream=stream)
-                k += 1
-                rec(k)
-            for name in ("K", "V"):
-                d = kv[name]
-                P.rptq_kv_dequant(d["packed"], C, d["R"], d["bounds"], d["s"], d["z"], kvb, out=d["out"],
-                                  stream=stream)
-                k += 1
-                rec(k)
+        for name in ("K", "V"):
+            d = kv[name]
+            P.rptq_kv_quant_pack(d["x"], d["R"], d["bounds"], d["s"], d["z"], kvb, out=d["packed"], stream=stream)
+            k += 1
+            rec(k)
+        for name in ("K", "V"):
+            d = kv[name]
+            P.rptq_kv_dequant(d["packed"], C, d["R"], d["bounds"], d["s"], d["z"], kvb, out=d["out"],
+                              stream=stream)
+            k += 1
+            rec(k)
 
     for _ in range(args.warmup):
         step()
@@ -201,15 +216,14 @@ def main():
                              gemm_tops=ops / t_gm / 1e12, gemm_frac_int8_peak=ops / t_gm / 1e12 / INT8_PEAK_TOPS,
                              ln_GBps=ln_bytes / t_ln / 1e9, ln_frac_hbm_peak=ln_bytes / t_ln / 1e9 / HBM_PEAK_GBPS)
     out = {}
-    if True:
-        kv_bytes = T * C * (2 + kvb / 8)
-        tq = (avg["kvq_K"] + avg["kvq_V"]) / 2
-        td = (avg["kvd_K"] + avg["kvd_V"]) / 2
-        out["kv_pack_GBps"] = kv_bytes / tq / 1e9
-        out["kv_pack_frac_hbm_peak"] = kv_bytes / tq / 1e9 / HBM_PEAK_GBPS
-        out["kv_dequant_GBps"] = kv_bytes / td / 1e9
-        out["kv_pack_ms"] = tq * 1e3
-        out["kv_dequant_ms"] = td * 1e3
+    kv_bytes = T * C * (2 + kvb / 8)
+    tq = (avg["kvq_K"] + avg["kvq_V"]) / 2
+    td = (avg["kvd_K"] + avg["kvd_V"]) / 2
+    out["kv_pack_GBps"] = kv_bytes / tq / 1e9
+    out["kv_pack_frac_hbm_peak"] = kv_bytes / tq / 1e9 / HBM_PEAK_GBPS
+    out["kv_dequant_GBps"] = kv_bytes / td / 1e9
+    out["kv_pack_ms"] = tq * 1e3
+    out["kv_dequant_ms"] = td * 1e3
 
     gemm_ops_launch = ops
     t_gemm = avg["gemm4"]
@@ -222,10 +236,9 @@ def main():
                  {"bound": "hbm", "kernel": "ln_reorder_quant_kernel<4,0>", "achieved": ln_bytes / avg["ln4"] / 1e9,
                   "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ln_bytes / avg["ln4"] / 1e9 / HBM_PEAK_GBPS,
                   "traffic": measured_traffic("ln_reorder_quant", ln_bytes)}]
-    if True:
-        rooflines.append({"bound": "hbm", "kernel": "kv_quant_pack_kernel<3>", "achieved": out["kv_pack_GBps"],
-                          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": out["kv_pack_frac_hbm_peak"],
-                          "traffic": measured_traffic("kv_quant_pack", T * C * (2 + kvb / 8))})
+    rooflines.append({"bound": "hbm", "kernel": "kv_quant_pack_kernel<3>", "achieved": out["kv_pack_GBps"],
+                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": out["kv_pack_frac_hbm_peak"],
+                      "traffic": measured_traffic("kv_quant_pack", T * C * (2 + kvb / 8))})
 
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
@@ -239,7 +252,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": elapsed / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8 MFMA (u4/u3 activation codes, s4 weights), fp32 LN/epilogue",
+        "dtype": "int8",
         "data": "synthetic (seeded per-channel N(mu_c, sigma_c) activations with 1% x100 outlier channels; "
                 "W ~ N(0, 0.02))",
         "config": {"workload": "OPT-66B fc1 layer W4A4 (+W4A3): LayerNorm(9216)+per-cluster quant -> "
@@ -261,6 +274,73 @@ def main():
     }
     print(json.dumps(line), flush=True)
 
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES // 2, dtype=torch.float16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {COPY_PROBE_BYTES} bytes read and written")
+
+
+# Kernels whose HBM traffic bench.py reports, matched on rocprofv3's kernel
+# names: the W4A4 GEMM, the 4-bit fused LayerNorm-quant, the 3-bit KV pack.
+PMC_KERNELS = {
+    "qgemm": "qgemm_kernel<4, 4, false",
+    "ln_reorder_quant": "ln_reorder_quant_kernel<4, 0,",
+    "kv_quant_pack": "kv_quant_pack_kernel<3,",
+}
+COPY_PROBE_BYTES = 1 << 30
+
+
+def _pmc_per_dispatch(path, counter):
+    """{dispatch id: (kernel name, counter value summed over its rows)} from a
+    rocprofv3 counter-collection CSV."""
+    import csv
+    out = {}
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            if r.get("Counter_Name") != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, v = out.get(d, (r["Kernel_Name"], 0.0))
+            out[d] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def ingest_pmc(fetch_csv, write_csv):
+    """HBM bytes per launch = FETCH_SIZE + WRITE_SIZE (KiB per dispatch), each
+    scaled so that the copy probe (the last copy dispatch of the run) reads
+    and writes exactly COPY_PROBE_BYTES."""
+    res = {}
+    scale = {}
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        d = _pmc_per_dispatch(path, counter)
+        copies = [k for k, (n, _) in d.items() if "copy" in n.lower()]
+        if not copies:
+            raise SystemExit(f"{path}: no copy dispatch (run bench.py with --copy-probe)")
+        probe = d[max(copies)][1] * 1024.0
+        scale[counter] = COPY_PROBE_BYTES / probe
+        per[counter] = d
+    for key, pat in PMC_KERNELS.items():
+        vals = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            v = [x for n, x in per[counter].values() if pat in n]
+            if not v:
+                break
+            vals[counter] = float(np.mean(v)) * 1024.0 * scale[counter]
+        if len(vals) == 2:
+            res[key] = {"source_hash": source_hash(KERNEL_SOURCES[key]),
+                        "bytes_per_launch": vals["FETCH_SIZE"] + vals["WRITE_SIZE"],
+                        "fetch_bytes": vals["FETCH_SIZE"], "write_bytes": vals["WRITE_SIZE"],
+                        "scale_fetch": scale["FETCH_SIZE"], "scale_write": scale["WRITE_SIZE"],
+                        "kernel_match": pat}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(res, fh, indent=1, sort_keys=True)
+    print(json.dumps(res, indent=1))
+
 
 def cpu_baseline(w, x_dev, gamma, beta, R, bounds, s, z, N, budget_s):
     """The oracle (plain C++/OpenMP, never tuned) on a bounded row sample of
@@ -269,12 +349,12 @@ def cpu_baseline(w, x_dev, gamma, beta, R, bounds, s, z, N, budget_s):
     `budget_s` seconds of CPU work."""
     import oracle as orc
     import synthetic
-    rows_x = x_dev[:64].cpu().numpy()
+    rows_x = x_dev[:4096].cpu().numpy()
     W = synthetic.weights(w.K, N, w.seed)
     Wq, s_w = orc.quantize_weights(W, w.w_bits)
     del W
     done, t_tot = 0, 0.0
-    chunk = 8
+    chunk = 32
     while t_tot < budget_s and done + chunk <= rows_x.shape[0]:
         xs = rows_x[done:done + chunk]
         t0 = time.perf_counter()
