@@ -154,6 +154,15 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid / WN, wn = wid % WN;
 
+    // cluster tables held one entry per lane (g <= 64) and read with readlane:
+    // no scalar memory loads (and their waits) inside the K loop.  The two
+    // vector loads complete here, before any prefetch is issued, so the
+    // memory-counter waits inside the loop never have to cover them.
+    const int lane_c = lane < ga.g ? lane : ga.g - 1;
+    const int end_l = ga.step_end[lane_c];
+    const float d_l = ga.scale[lane_c];
+    asm volatile("" ::"v"(end_l), "v"(d_l) : "memory");
+
     // ---- staging: piece p = tid + i * NT covers row p / SK, step p % SK of a stage
     uint32_t a_voff[PA], b_voff[PB];
     int a_lds[PA], b_lds[PB], a_step[PA], b_step[PB];
@@ -176,7 +185,11 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     const int64_t a_left = (M - m0) * a_row_bytes;
     const int64_t b_left = (int64_t)(N - n0) * b_row_bytes;
     const int nsteps = ga.nsteps;
-    const int nst = (nsteps + SK - 1) / SK;
+    // stages, rounded up to an even count so the loop below always runs
+    // whole pairs (a padding stage reads zero pieces and adds nothing); a
+    // loop exit between the two halves would make the compiler's
+    // memory-counter waits at the loop head conservative
+    const int nst = ((nsteps + SK - 1) / SK + 1) & ~1;
 
     // Pieces of steps past the end of K read as zero (offset beyond the
     // buffer), so the MFMAs of a partial last stage add nothing.
@@ -230,11 +243,6 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     const int a_frag = (wm * 64 + (lane & 31)) * LDSS + (lane >> 5) * 16;
     const int b_frag = (wn * 64 + (lane & 31)) * LDSS + (lane >> 5) * 16;
 
-    // cluster tables held one entry per lane (g <= 64) and read with readlane:
-    // no scalar memory loads (and their waits) inside the K loop
-    const int lane_c = lane < ga.g ? lane : ga.g - 1;
-    const int end_l = ga.step_end[lane_c];
-    const float d_l = ga.scale[lane_c];
     int c = 0, c_end = __builtin_amdgcn_readfirstlane(end_l);
 
     auto flush = [&](int cl) {
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     // stage's staging registers `nxt` is unpacked into the other buffer in
     // the same instruction stream (on the last stage that buffer is never
     // read again, so the stores are harmless).
-    auto compute = [&](int buf, int st, const Stage& nxt) {
+    auto compute = [&](int buf, int st, Stage& nxt) {
         v4i af[2][2], bf[2][2];
         auto rd = [&](int slot, int ks) {
 #pragma unroll
@@ -287,6 +295,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
             if (ks < NPIECE) put(nxt, buf ^ 1, ks);    // unused on the last stage
+            if (ks == NPIECE - 1) gload(nxt, st + 3);   // the set is free again: two stages ahead
             // issue order inside the step: each MFMA is followed by part of
             // the next step's fragment reads, the unpack VALU work, and last
             // the staging stores (so the reads never wait behind them)
@@ -309,21 +318,20 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
         }
     };
 
-    // ---- pipeline: register set R[st & 1] is free at the start of stage st
-    // and receives stage st + 2; R[(st + 1) & 1] holds stage st + 1, which is
-    // unpacked into LDS during stage st.  One barrier per stage.
+    // ---- pipeline: during stage st, register set R[(st + 1) & 1] holds
+    // stage st + 1, which is unpacked into the other LDS buffer and then
+    // reloaded with stage st + 3; R[st & 1] has stage st + 2 in flight.  Every
+    // load thus has about two stages to arrive.  One barrier per stage.
     Stage R0, R1;
     gload(R0, 0);
-    if (nst > 1) gload(R1, 1);
+    gload(R1, 1);
 #pragma unroll
     for (int k = 0; k < NPIECE; ++k) put(R0, 0, k);
+    gload(R0, 2);
     __syncthreads();
     for (int st = 0; st < nst; st += 2) {
-        if (st + 2 < nst) gload(R0, st + 2);
         compute(0, st, R1);
         __syncthreads();
-        if (st + 1 >= nst) break;
-        if (st + 3 < nst) gload(R1, st + 3);
         compute(1, st + 1, R0);
         __syncthreads();
     }
