@@ -269,13 +269,35 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
             }
     };
 
-    // One stage: 4 MFMA steps from LDS buffer `buf`; the fragments of step
+    // Fragments: slot 0 holds the even steps, slot 1 the odd ones.  The
+    // MFMAs of a stage's last step are deferred past the barrier: they need
+    // only registers and cover the latency of the next stage's first
+    // fragment reads, which cannot be issued before it.  (Slot 1 starts at
+    // zero, so the deferred MFMAs before stage 0 add nothing.)
+    v4i af[2][2], bf[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) af[1][i] = (v4i)0;
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[slot][i], bf[slot][j], acc[i][j], 0, 0, 0);
+    };
+    auto flush_if_end = [&](int steps_done) {
+        if (steps_done == c_end) {
+            flush(c);
+            ++c;
+            c_end = c < ga.g ? __builtin_amdgcn_readlane(end_l, c) : 0x7fffffff;
+        }
+    };
+
+    // One stage: SK MFMA steps from LDS buffer `buf`; the fragments of step
     // ks + 1 are read before the MFMAs of step ks, and piece ks of the next
     // stage's staging registers `nxt` is unpacked into the other buffer in
     // the same instruction stream (on the last stage that buffer is never
     // read again, so the stores are harmless).
     auto compute = [&](int buf, int st, Stage& nxt) {
-        v4i af[2][2], bf[2][2];
         auto rd = [&](int slot, int ks) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -285,15 +307,14 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
                 bf[slot][j] = *reinterpret_cast<const v4i*>(&Bs[buf][b_frag + j * 32 * LDSS + ks * 32]);
         };
         rd(0, 0);
+        mfmas(1);                                  // last step of stage st - 1
+        flush_if_end(st * SK);
+        const bool last = st + 1 == nst;
 #pragma unroll
         for (int ks = 0; ks < SK; ++ks) {
             const int cur = ks & 1;
             if (ks + 1 < SK) rd(cur ^ 1, ks + 1);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
+            if (ks + 1 < SK || last) mfmas(cur);
             if (ks < NPIECE) put(nxt, buf ^ 1, ks);    // unused on the last stage
             if (ks == NPIECE - 1) gload(nxt, st + 3);   // the set is free again: two stages ahead
             // issue order inside the step: each MFMA is followed by part of
@@ -310,11 +331,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-            if (st * SK + ks + 1 == c_end) {
-                flush(c);
-                ++c;
-                c_end = c < ga.g ? __builtin_amdgcn_readlane(end_l, c) : 0x7fffffff;
-            }
+            if (ks + 1 < SK || last) flush_if_end(st * SK + ks + 1);
         }
     };
 
