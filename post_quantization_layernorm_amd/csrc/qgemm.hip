@@ -10,25 +10,27 @@
 //   Y[m][n] = s_w[n] * sum_c s_c * (acc_c[m][n] - z_c * colsum_c[n]),
 //   acc_c   = sum over the cluster's K-segment of q * W'   (int32, exact).
 //
-// Design (one 512-thread workgroup per CU, 8 waves, 2 per SIMD so one wave's
-// VALU work overlaps the other's MFMAs):
-//   - 256 x 128 output tile, waves in a 4 x 2 grid of 64 x 64, each wave a
+// Design (two 256-thread workgroups per CU, 4 waves each, so every SIMD runs
+// two waves whose VALU work overlaps the other's MFMAs, and one workgroup's
+// barrier waits are covered by the other's MFMAs):
+//   - 128 x 128 output tile, waves in a 2 x 2 grid of 64 x 64, each wave a
 //     2 x 2 grid of v_mfma_i32_32x32x32_i8 tiles;
 //   - K advances in stages of 128 codes (4 MFMA steps of 32).  Clusters are
 //     padded to multiples of 32 codes, so a step never straddles clusters;
 //   - A (3/4/8-bit activation codes) and W' (4/8-bit weights) are fetched
 //     packed with buffer loads (scalar stage offsets; rows past M or N read
-//     as zero), two stages ahead of the MFMAs, unpacked to int8 in registers
-//     and staged in a double-buffered LDS tile (row stride 144 B: the 16-byte
-//     fragment reads of 8 consecutive lanes hit disjoint banks);
+//     as zero) about two stages ahead and staged in a double-buffered LDS
+//     tile.  W' is unpacked to int8 on the way in (row stride 144 B: the
+//     16-byte fragment reads of 8 consecutive lanes hit disjoint banks);
+//     4-bit codes stay packed in LDS (half the store bytes) and each wave
+//     unpacks its own fragments after reading them; 3/8-bit codes are
+//     unpacked on the way in.  The next stage's staging is interleaved with
+//     the current stage's MFMAs, and each stage's last MFMA step is deferred
+//     past the barrier to cover the next stage's first fragment reads;
 //   - one running int32 accumulator per MFMA tile for the whole K loop: at
 //     the last step of cluster c it is converted and added to fp32 out with
 //     weight d_c = s_c - s_(c+1) (summation by parts of sum_c s_c acc_c), so
 //     the accumulators are never reset and every step is the same code;
-//   - the next stage's staging (unpack + LDS store of one piece per step) is
-//     interleaved with the current stage's MFMAs: LDS stores are the scarce
-//     LDS resource on gfx950 (~75 B/clk/CU against ~220 B/clk/CU for
-//     16-byte reads);
 //   - 8-bit codes q are staged as q - 128 (signed MFMA operands) and 4-bit
 //     weights as 16 * w (nibble moved to the high half of the byte, sign for
 //     free); both are undone exactly: s_c / 16 in the scale, and
@@ -43,6 +45,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 constexpr int GROUP_M = 8;
@@ -134,7 +137,13 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     constexpr int PA = CFG::PA, PB = CFG::PB, WN = CFG::WN;
     constexpr int NPIECE = PA + PB;
     static_assert(NPIECE <= SK, "one staged piece per step");
-    __shared__ __align__(16) int8_t As[2][BM * LDSS];
+    // 4-bit codes stay packed in LDS (rows of SK * 16 bytes, padded to
+    // SK * 16 + 8 so that the 8-byte fragment reads of 32 consecutive lanes
+    // hit 64 distinct banks) and are unpacked by each wave after reading
+    // its fragments: half the LDS store bytes of the unpacked tile
+    constexpr bool APACK = ABITS == 4;
+    constexpr int ALDSS = APACK ? SK * 16 + 8 : LDSS;
+    __shared__ __align__(16) int8_t As[2][BM * ALDSS];
     __shared__ __align__(16) int8_t Bs[2][BN * LDSS];
     constexpr int APIECE = 4 * ABITS, BPIECE = 4 * WBITS;           // bytes per 32 codes
 
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     for (int i = 0; i < PA; ++i) {
         const int p = tid + i * NT, row = p / SK, part = p % SK;
         a_voff[i] = (uint32_t)(row * a_row_bytes + part * APIECE);
-        a_lds[i] = row * LDSS + part * 32;
+        a_lds[i] = row * ALDSS + part * (APACK ? 16 : 32);
         a_step[i] = part;
     }
 #pragma unroll
@@ -208,8 +217,14 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     auto put = [&](const Stage& S, int buf, int k) {
         uint32_t o[8];
         if (k < PA) {
-            unpack_act<ABITS>(S.a[k], o);
-            store32(&As[buf][a_lds[k]], o);
+            if constexpr (APACK) {
+                int8_t* p = &As[buf][a_lds[k]];
+                reinterpret_cast<u32x2*>(p)[0] = u32x2{S.a[k][0], S.a[k][1]};
+                reinterpret_cast<u32x2*>(p)[1] = u32x2{S.a[k][2], S.a[k][3]};
+            } else {
+                unpack_act<ABITS>(S.a[k], o);
+                store32(&As[buf][a_lds[k]], o);
+            }
         } else {
             unpack_wgt<WBITS>(S.b[k - PA], o);
             store32(&Bs[buf][b_lds[k - PA]], o);
@@ -240,7 +255,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
 
     // accumulator register r of this lane holds row (r/4)*8 + (lane/32)*4 + r%4, column lane%32
     const int row_l = (lane >> 5) * 4, col_l = lane & 31;
-    const int a_frag = (wm * 64 + (lane & 31)) * LDSS + (lane >> 5) * 16;
+    const int a_frag = (wm * 64 + (lane & 31)) * ALDSS + (lane >> 5) * (APACK ? 8 : 16);
     const int b_frag = (wn * 64 + (lane & 31)) * LDSS + (lane >> 5) * 16;
 
     int c = 0, c_end = __builtin_amdgcn_readfirstlane(end_l);
@@ -301,7 +316,16 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
         auto rd = [&](int slot, int ks) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                af[slot][i] = *reinterpret_cast<const v4i*>(&As[buf][a_frag + i * 32 * LDSS + ks * 32]);
+            {
+                if constexpr (APACK) {
+                    // 16 packed codes (byte i = c_i | c_(4+i) << 4) -> 16 int8 in code order
+                    const u32x2 d = *reinterpret_cast<const u32x2*>(&As[buf][a_frag + i * 32 * ALDSS + ks * 16]);
+                    af[slot][i] = v4i{(int)(d.x & 0x0F0F0F0Fu), (int)((d.x >> 4) & 0x0F0F0F0Fu),
+                                      (int)(d.y & 0x0F0F0F0Fu), (int)((d.y >> 4) & 0x0F0F0F0Fu)};
+                } else {
+                    af[slot][i] = *reinterpret_cast<const v4i*>(&As[buf][a_frag + i * 32 * LDSS + ks * 32]);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 bf[slot][j] = *reinterpret_cast<const v4i*>(&Bs[buf][b_frag + j * 32 * LDSS + ks * 32]);
@@ -371,7 +395,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     }
 }
 
-using Cfg = TileCfg<256, 128, 8, 4, 1>;
+using Cfg = TileCfg<128, 128, 4, 4, 2>;
 
 template <int ABITS, int WBITS>
 const void* pick2(bool debug) {
