@@ -62,8 +62,8 @@ __global__ __launch_bounds__(kMaxBlock) void kv_quant_pack_kernel(
     auto process = [&](u32x4 (&buf)[CH], int64_t t) {
         put_row_chunks<true, CH>(xrow, buf);
         __syncthreads();
-        if (t + 2 * (int64_t)gridDim.x < T)
-            load_row_chunks<true, CH>(buf, kv + (t + 2 * (int64_t)gridDim.x) * C, in_bytes);
+        const int64_t tn = t + 2 * (int64_t)gridDim.x;
+        load_row_chunks<true, CH>(buf, kv + tn * C, tn < T ? in_bytes : 0);
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
             int q[8];
@@ -75,16 +75,19 @@ __global__ __launch_bounds__(kMaxBlock) void kv_quant_pack_kernel(
             store_unit_at<BITS>(orow + uob[u], q);
         }
         __syncthreads();
-        store_row_chunks<OVEC16, OCH>(packed + t * row_bytes, row_bytes, orow);
+        store_row_chunks<OVEC16, OCH>(packed + t * row_bytes, t < T ? row_bytes : 0, orow);
     };
 
+    // Whole pairs of rows: a row at or past T reads zeros and drops its
+    // stores, so no load or store is conditional and the compiler's
+    // memory-counter waits stay exact.
     const int64_t G = gridDim.x;
     int64_t t = blockIdx.x;
-    if (t < T) load_row_chunks<true, CH>(bufA, kv + t * C, in_bytes);
-    if (t + G < T) load_row_chunks<true, CH>(bufB, kv + (t + G) * C, in_bytes);
+    load_row_chunks<true, CH>(bufA, kv + t * C, t < T ? in_bytes : 0);
+    __builtin_amdgcn_sched_barrier(0);      // keep the two rows' loads in this order
+    load_row_chunks<true, CH>(bufB, kv + (t + G) * C, t + G < T ? in_bytes : 0);
     for (; t < T; t += 2 * G) {
         process(bufA, t);
-        if (t + G >= T) break;
         process(bufB, t + G);
     }
 }
@@ -130,8 +133,8 @@ __global__ __launch_bounds__(kMaxBlock) void kv_dequant_kernel(
     auto process = [&](chunk_t<VEC16> (&buf)[CH], int64_t t) {
         put_row_chunks<VEC16, CH>(prow, buf);
         __syncthreads();
-        if (t + 2 * (int64_t)gridDim.x < T)
-            load_row_chunks<VEC16, CH>(buf, packed + (t + 2 * (int64_t)gridDim.x) * row_bytes, row_bytes);
+        const int64_t tn = t + 2 * (int64_t)gridDim.x;
+        load_row_chunks<VEC16, CH>(buf, packed + tn * row_bytes, tn < T ? row_bytes : 0);
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
             int q[8];
@@ -145,16 +148,16 @@ __global__ __launch_bounds__(kMaxBlock) void kv_dequant_kernel(
             }
         }
         __syncthreads();
-        store_row_chunks<true, OCH>(out + t * C, out_bytes, orow);
+        store_row_chunks<true, OCH>(out + t * C, t < T ? out_bytes : 0, orow);
     };
 
     const int64_t G = gridDim.x;
     int64_t t = blockIdx.x;
-    if (t < T) load_row_chunks<VEC16, CH>(bufA, packed + t * row_bytes, row_bytes);
-    if (t + G < T) load_row_chunks<VEC16, CH>(bufB, packed + (t + G) * row_bytes, row_bytes);
+    load_row_chunks<VEC16, CH>(bufA, packed + t * row_bytes, t < T ? row_bytes : 0);
+    __builtin_amdgcn_sched_barrier(0);      // keep the two rows' loads in this order
+    load_row_chunks<VEC16, CH>(bufB, packed + (t + G) * row_bytes, t + G < T ? row_bytes : 0);
     for (; t < T; t += 2 * G) {
         process(bufA, t);
-        if (t + G >= T) break;
         process(bufB, t + G);
     }
 }

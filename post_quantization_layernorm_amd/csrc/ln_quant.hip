@@ -40,20 +40,6 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
     return t;
 }
 
-// Two sums over the workgroup in one exchange (one pair of barriers).
-__device__ __forceinline__ void block_sum2(float& a, float& b, float* scratch) {
-    a = wave_sum(a);
-    b = wave_sum(b);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    if (lane == 0) { scratch[2 * w] = a; scratch[2 * w + 1] = b; }
-    __syncthreads();
-    float ta = 0.0f, tb = 0.0f;
-    for (int i = 0; i < nw; ++i) { ta += scratch[2 * i]; tb += scratch[2 * i + 1]; }
-    __syncthreads();
-    a = ta;
-    b = tb;
-}
-
 template <int BITS, int MODE, int UPL>
 __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
     const void* __restrict__ xin, int64_t M, int32_t K, int64_t row_bytes,
@@ -81,65 +67,72 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
     const int nchunks = row_in_bytes / 16;
 
     // ---- per-lane unit tables (fixed for every row); idle units gather
-    // element 0 and write to the dummy slot
+    // element 0 and write to the dummy slot.  A padding position (past its
+    // cluster's end) gets gamma 0 and beta -FLT_MAX, so its code saturates to
+    // 0 without a select (in quant-only mode its value is replaced the same way).
+    constexpr float kPad = -3.0e38f;
     int src[UPL][8];
     float gam[UPL][8], bet[UPL][8];
-    float uinv[UPL];
-    int uzb[UPL], unv[UPL], uob[UPL];
+    float uinv[UPL], uzf[UPL];
+    int uob[UPL];
 #pragma unroll
     for (int u = 0; u < UPL; ++u) {
         const int unit = tid + u * BLOCK;
-        unv[u] = 0;
         uinv[u] = 0.0f;
-        uzb[u] = 0;
+        uzf[u] = 0.0f;
         uob[u] = (int)(dummy - orow);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { src[u][e] = 0; gam[u][e] = 0.0f; bet[u][e] = 0.0f; }
+        for (int e = 0; e < 8; ++e) { src[u][e] = 0; gam[u][e] = 0.0f; bet[u][e] = kPad; }
         if (unit < n_units) {
             const int p0 = UnitGeom<BITS>::first(unit);
             const int c = cluster_of_padded(ca, p0);
             const int n_c = ca.bounds[c + 1] - ca.bounds[c];
             uinv[u] = ca.inv_s[c];
-            uzb[u] = ca.z[c] - kRoundMagicBits;
+            uzf[u] = (float)ca.z[c];               // |z| <= 2^21: exact
             uob[u] = UnitGeom<BITS>::out_byte(unit);
-            int nv = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = p0 + e * UnitGeom<BITS>::stride - ca.off[c];
                 if (i < n_c) {
                     const int j = ca.bounds[c] + i;
-                    nv = e + 1;
                     if constexpr (LN) {
                         src[u][e] = (R ? R[j] : j) * 2;
                         gam[u][e] = gamma_r[j];
                         bet[u][e] = beta_r[j];
                     } else {
                         src[u][e] = j * 4;
+                        gam[u][e] = 1.0f;
+                        bet[u][e] = 0.0f;
                     }
                 }
             }
-            unv[u] = nv;
         }
     }
+    const float qhi = kRoundMagic + (float)QMAX;
 
-    // Two register buffers: while row r (in one) is processed, row r + G is
-    // in flight in the other (G = gridDim.x).
+    // Two register buffers: while row r (in one) is processed, rows r + G and
+    // r + 2G are in flight (G = gridDim.x).  Rows at or past M are read as
+    // zeros and their stores dropped (descriptor of zero bytes), so every
+    // workgroup runs whole pairs of rows and no load or store is conditional.
     u32x4 bufA[CH], bufB[CH];
     auto load_row = [&](u32x4 (&buf)[CH], int64_t row) {
         const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(static_cast<const uint8_t*>(xin) + row * row_in_bytes, row_in_bytes);
+            make_rsrc(static_cast<const uint8_t*>(xin) + row * row_in_bytes, row < M ? row_in_bytes : 0);
 #pragma unroll
         for (int i = 0; i < CH; ++i)
             buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(tid + i * BLOCK) * 16u, 0, 0);
     };
 
+    // Two barriers per row: (1) the row and the per-wave partial sums are in
+    // LDS; (2) the packed output row is in LDS (and every lane is done
+    // reading the input row and the partial sums).
+    const int lane = tid & 63, wv = tid >> 6, nw = BLOCK >> 6;
     auto process = [&](u32x4 (&buf)[CH], int64_t row) {
-        float mean = 0.0f, rstd = 0.0f;
+        float s1 = 0.0f, s2 = 0.0f;
         if constexpr (LN) {
             // sum x and sum x^2 from packed fp16 dot products (exact
             // products, fp32 accumulation); chunks past the row are zeros
             const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
-            float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
                 const uint32_t w[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
@@ -150,7 +143,18 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
                     s2 = __builtin_amdgcn_fdot2(h, h, s2, false);
                 }
             }
-            block_sum2(s1, s2, red);
+            s1 = wave_sum(s1);
+            s2 = wave_sum(s2);
+            if (lane == 0) { red[2 * wv] = s1; red[2 * wv + 1] = s2; }
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) reinterpret_cast<u32x4*>(xrow)[tid + i * BLOCK] = buf[i];
+        __syncthreads();
+
+        float mean = 0.0f, rstd = 0.0f;
+        if constexpr (LN) {
+            s1 = 0.0f; s2 = 0.0f;
+            for (int i = 0; i < nw; ++i) { s1 += red[2 * i]; s2 += red[2 * i + 1]; }
             const float m1 = s1 / (float)K, m2 = s2 / (float)K;
             float var = m2 - m1 * m1;
             mean = m1;
@@ -171,20 +175,17 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
                         }
                     }
                 }
-                ss = block_sum(ss, red);
+                ss = block_sum(ss, red + 32);
                 var = ss / (float)K;
             }
             rstd = 1.0f / __builtin_sqrtf(var + eps);
         }
-#pragma unroll
-        for (int i = 0; i < CH; ++i) reinterpret_cast<u32x4*>(xrow)[tid + i * BLOCK] = buf[i];
-        __syncthreads();
-        if (row + 2 * (int64_t)gridDim.x < M) load_row(buf, row + 2 * (int64_t)gridDim.x);
+        load_row(buf, row + 2 * (int64_t)gridDim.x);
 
         const float nmr = -mean * rstd;
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
-            int q[8];
+            uint32_t qb[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float y;
@@ -193,25 +194,27 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
                     const float n = __builtin_fmaf(xv, rstd, nmr);
                     y = __builtin_fmaf(gam[u][e], n, bet[u][e]);
                 } else {
-                    y = *reinterpret_cast<const float*>(xrow + src[u][e]);
+                    y = __builtin_fmaf(gam[u][e], *reinterpret_cast<const float*>(xrow + src[u][e]), bet[u][e]);
                 }
-                const int qq = quant_code(y, uinv[u], uzb[u], QMAX);
-                q[e] = e < unv[u] ? qq : 0;
+                qb[e] = quant_bits(y, uinv[u], uzf[u], qhi);
             }
-            store_unit_at<BITS>(orow + uob[u], q);
+            store_unit_bits<BITS>(orow + uob[u], qb);
         }
         __syncthreads();
         // 3-bit rows are a multiple of 12 bytes: 4-byte stores
-        store_row_chunks<BITS != 3, chunks_for<BITS != 3>(UPL * BITS)>(codes + row * row_bytes, row_bytes, orow);
+        store_row_chunks<BITS != 3, chunks_for<BITS != 3>(UPL * BITS)>(codes + row * row_bytes,
+                                                                       row < M ? row_bytes : 0, orow);
     };
 
     const int64_t G = gridDim.x;
     int64_t row = blockIdx.x;
-    if (row < M) load_row(bufA, row);
-    if (row + G < M) load_row(bufB, row + G);
+    // (the second buffer is loaded first, matching the order in which the
+    // loop body issues its prefetches, so the compiler's memory-counter
+    // waits stay exact)
+    load_row(bufB, row + G);
+    load_row(bufA, row);
     for (; row < M; row += 2 * G) {
         process(bufA, row);
-        if (row + G >= M) break;
         process(bufB, row + G);
     }
 }
@@ -245,7 +248,7 @@ hipError_t launch_ln_reorder_quant(const void* x, int in_mode, int64_t M, int32_
     if (!k) return hipErrorInvalidValue;
     const int esz = in_mode == RPTQ_IN_FP16_RAW ? 2 : 4;
     const int ch = upl * esz / 2, och = (upl * ca.bits + 15) / 16;
-    const size_t lds = (size_t)ch * 16 * block + (size_t)och * 16 * block + 16 + 128;
+    const size_t lds = (size_t)ch * 16 * block + (size_t)och * 16 * block + 16 + 256;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;

@@ -36,6 +36,19 @@ __device__ __forceinline__ int quant_code(float v, float inv_s, int zb, int qmax
     return __builtin_elementwise_max(__builtin_elementwise_min(k, qmax), 0);
 }
 
+// The same code, left in the low bits of a float's bit pattern: with
+// zf = (float)z and hi = 1.5*2^23 + qmax,
+//   u = fl(v * inv_s + 1.5*2^23)    the exact product rounded once to an
+//                                   integer (ties to even: 1.5*2^23 is even)
+//   u + zf                          exact (integers below 2^24)
+//   clamp to [1.5*2^23, hi]         saturates both ways, q = bits - bits(1.5*2^23)
+// The low 22 bits of the result are q (the constant's are zero), so packing
+// can take the code's byte without masking.
+__device__ __forceinline__ uint32_t quant_bits(float v, float inv_s, float zf, float hi) {
+    const float u = __builtin_fmaf(v, inv_s, kRoundMagic) + zf;
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(u, kRoundMagic, hi));
+}
+
 // Wave64 sum.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -97,6 +110,28 @@ __device__ __forceinline__ void store_unit_at(unsigned char* p, const int (&q)[8
 template <int BITS>
 __device__ __forceinline__ void store_unit(unsigned char* out, int unit, const int (&q)[8]) {
     store_unit_at<BITS>(out + UnitGeom<BITS>::out_byte(unit), q);
+}
+
+// Pack the 8 codes of a unit given as quant_bits results (low bits = code)
+// and store them at p (LDS), in the layout of store_unit_at.
+template <int BITS>
+__device__ __forceinline__ void store_unit_bits(unsigned char* p, const uint32_t (&b)[8]) {
+    // byte 0 of each of four words -> one word (v_perm_b32 picks bytes of
+    // its two sources; selector 0x0c yields a zero byte)
+    auto gather4 = [](uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+        return __builtin_amdgcn_perm(w1, w0, 0x0C0C0400u) | __builtin_amdgcn_perm(w3, w2, 0x04000C0Cu);
+    };
+    if constexpr (BITS == 8) {
+        *reinterpret_cast<uint2*>(p) = uint2{gather4(b[0], b[1], b[2], b[3]), gather4(b[4], b[5], b[6], b[7])};
+    } else if constexpr (BITS == 4) {
+        const uint32_t lo = gather4(b[0], b[1], b[2], b[3]), hi = gather4(b[4], b[5], b[6], b[7]);
+        *reinterpret_cast<uint32_t*>(p) = lo | hi << 4;
+    } else {
+        int q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = (int)(b[e] & 7u);
+        store_unit_at<3>(p, q);
+    }
 }
 
 // Row transfers with buffer instructions that every lane executes (accesses
