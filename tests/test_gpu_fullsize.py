@@ -1,0 +1,117 @@
+"""GPU parity at the full benchmark sizes, in the launch configurations the
+benchmark times: the OPT-66B fc1 layer (16384 tokens x 9216 -> 36864, g = 32,
+W4A4 and W4A3) and the OPT-66B K/V cache (524288 tokens x 9216 channels,
+3 bit).  The device runs every row; the oracle checks sampled rows one by one
+(its cost grows with the sample, not with the launch).  All parameters (R,
+bounds, s, z, Wq) come from the oracle's calibration."""
+import numpy as np
+import pytest
+
+import oracle as orc
+import synthetic
+from helpers import dev, rel_l2
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def P():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import post_quantization_layernorm_amd as P
+    P.lib()
+    return P
+
+
+def _say(*a):
+    print("[fullsize]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def fc1():
+    """OPT-66B fc1 layer: inputs from the synthetic generator, parameters from
+    the oracle's calibration (3 KMeans restarts to keep the CPU time short)."""
+    w = synthetic.WORKLOADS["opt66b_fc1_w4a4"]
+    M, K, N, g = w.M, w.K, w.N, w.g
+    _say("generating", M, K, N)
+    mu, sg = synthetic.channel_params(K, w.seed, w.outlier_frac)
+    gamma, beta = synthetic.ln_params(K, w.seed, random=True)
+    xc = synthetic.tokens(w.calib_tokens, mu, sg, w.seed, synthetic.STREAM_CALIB)
+    mx, mn = orc.channel_minmax(orc.layernorm(xc, gamma, beta))
+    x = synthetic.tokens(M, mu, sg, w.seed, synthetic.STREAM_EVAL)
+    Wq, s_w = orc.quantize_weights(synthetic.weights(K, N, w.seed), w.w_bits)
+    u = synthetic.kmeans_uniforms(w.seed, 3, g)
+    params = {}
+    for ab in (4, 3):
+        params[ab] = orc.calibrate(mx, mn, g, ab, u, n_init=3)
+    _say("calibrated")
+    return dict(M=M, K=K, N=N, g=g, x=x, gamma=gamma, beta=beta, Wq=Wq, s_w=s_w, params=params)
+
+
+ROWS = np.array([0, 1, 255, 256, 4097, 9000, 16382, 16383])
+
+
+@pytest.mark.parametrize("ab", [4, 3])
+def test_fc1_fullsize_ln_quant_sampled(P, fc1, ab):
+    M, K = fc1["M"], fc1["K"]
+    R, bounds, s, z = fc1["params"][ab]
+    _say("ln", ab)
+    xd = dev(fc1["x"].view(np.int16)).view(torch.float16)
+    codes = P.rptq_ln_reorder_quant(xd, dev(R), dev(fc1["gamma"][R]), dev(fc1["beta"][R]), bounds, s, z, ab)
+    got = codes[torch.from_numpy(ROWS).cuda()].cpu().numpy()
+    want = orc.ln_reorder_quant(fc1["x"][ROWS], fc1["gamma"], fc1["beta"], 1e-5, R, bounds, s, z, ab)
+    qg, pad = orc.unpack_seg32(got, K, bounds, ab, return_pad=True)
+    qw = orc.unpack_seg32(want, K, bounds, ab)
+    d = np.abs(qg.astype(np.int32) - qw.astype(np.int32))
+    assert not pad.any()
+    assert d.max() <= 1 and (d > 0).mean() <= 1e-3, (d.max(), (d > 0).mean())
+
+
+@pytest.mark.parametrize("ab", [4, 3])
+def test_fc1_fullsize_gemm_sampled(P, fc1, ab):
+    M, K, N, g = fc1["M"], fc1["K"], fc1["N"], fc1["g"]
+    R, bounds, s, z = fc1["params"][ab]
+    _say("gemm", ab)
+    # every row's codes from the oracle, so Y isolates the GEMM
+    codes_o = orc.ln_reorder_quant(fc1["x"], fc1["gamma"], fc1["beta"], 1e-5, R, bounds, s, z, ab)
+    wp, cs = P.rptq_pack_weights(fc1["Wq"], R, bounds, 4)
+    wp, cs, sw = dev(wp), dev(cs), dev(fc1["s_w"])
+    cd = dev(codes_o)
+    Y = P.rptq_qgemm(cd, M, K, N, bounds, s, z, ab, wp, 4, sw, cs)
+    Ys = Y[torch.from_numpy(ROWS).cuda()].cpu().numpy()
+    del Y
+    q = orc.unpack_seg32(codes_o[ROWS], K, bounds, ab)
+    Y_o, acc_o = orc.qgemm(q, fc1["Wq"], R, bounds, s, z, fc1["s_w"], return_acc=True)
+    assert rel_l2(Ys, Y_o) <= 1e-3
+    for i in range(len(ROWS)):
+        assert rel_l2(Ys[i], Y_o[i]) <= 1e-3, i
+    # int32 accumulators bit-exact over full K and N on a 64-row slice (a
+    # full-size debug buffer would be g x M x N x 4 bytes)
+    r0 = 4096
+    acc = torch.zeros((g, 64, N), dtype=torch.int32, device="cuda")
+    P.rptq_qgemm(cd[r0:r0 + 64], 64, K, N, bounds, s, z, ab, wp, 4, sw, cs, acc_debug=acc)
+    q64 = orc.unpack_seg32(codes_o[r0:r0 + 64], K, bounds, ab)
+    _, acc64 = orc.qgemm(q64, fc1["Wq"], R, bounds, s, z, fc1["s_w"], return_acc=True)
+    assert np.array_equal(acc.cpu().numpy(), acc64)
+
+
+def test_kv_fullsize_sampled(P):
+    kw = synthetic.KV_WORKLOADS["opt66b_kv_a3"]
+    T, C, g, bits = kw.T, kw.C, kw.g, kw.bits
+    _say("kv", T, C)
+    mu, sg = synthetic.channel_params(C, kw.seed, kw.outlier_frac, stream=synthetic.STREAM_CHANNELS)
+    kc = synthetic.tokens(kw.calib_tokens, mu, sg, kw.seed, synthetic.STREAM_CALIB)
+    mx, mn = orc.channel_minmax(kc)
+    R, bounds, s, z = orc.calibrate(mx, mn, g, bits, synthetic.kmeans_uniforms(kw.seed, 3, g), n_init=3)
+    kv = synthetic.tokens_device(T, mu, sg, kw.seed, synthetic.STREAM_EVAL)
+    packed = P.rptq_kv_quant_pack(kv, dev(R), bounds, s, z, bits)
+    out = P.rptq_kv_dequant(packed, C, dev(R), bounds, s, z, bits)
+    rows = np.array([0, 1, 8191, 8192, 262143, 400000, T - 2, T - 1])
+    ri = torch.from_numpy(rows).cuda()
+    x_rows = kv[ri].cpu().numpy().view(np.uint16)
+    want_p = orc.kv_quant_pack(x_rows, R, bounds, s, z, bits)
+    assert np.array_equal(packed[ri].cpu().numpy(), want_p)
+    want_d = orc.kv_dequant(want_p, C, R, bounds, s, z, bits)
+    assert np.array_equal(out[ri].cpu().numpy().view(np.uint16), want_d)

@@ -126,18 +126,21 @@ def test_ln_fused_codes_within_tolerance(P, bits, shape):
 
 
 def test_ln_fused_edge_rows(P):
-    """M = 1, a constant row (zero variance), identity R, single cluster."""
+    """M = 1, a constant row (zero variance), rows whose mean dwarfs their
+    spread (the kernel's exact second pass), identity R, single cluster."""
     K = 256
-    x = np.full((3, K), 7.0, np.float16)
+    x = np.full((5, K), 7.0, np.float16)
     x[1] = np.linspace(-100, 100, K).astype(np.float16)
     x[2, ::2] = -3.0
+    x[3] = (300.0 + np.random.default_rng(3).normal(0, 0.5, K)).astype(np.float16)
+    x[4] = (-1000.0 + np.where(np.arange(K) % 2, 0.5, -0.5)).astype(np.float16)
     gamma, beta = synthetic.ln_params(K, 3)
     bounds = np.array([0, K], np.int32)
     y = orc.layernorm(x, gamma, beta)
     mx, mn = orc.channel_minmax(y)
     s, z = orc.cluster_params(mx, mn, None, bounds, 4)
     want = orc.ln_reorder_quant(x, gamma, beta, 1e-5, None, bounds, s, z, 4)
-    for M in (1, 3):
+    for M in (1, 5):
         got = P.rptq_ln_reorder_quant(dev(x[:M].view(np.int16)).view(torch.float16), None, dev(gamma), dev(beta),
                                       bounds, s, z, 4).cpu().numpy()
         qg = orc.unpack_seg32(got, K, bounds, 4).astype(np.int32)
