@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
             make_rsrc(static_cast<const uint8_t*>(xin) + row * row_in_bytes, row < M ? row_in_bytes : 0);
 #pragma unroll
         for (int i = 0; i < CH; ++i)
-            buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(tid + i * BLOCK) * 16u, 0, 0);
+            buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(tid + i * BLOCK) * 16u, 0, kStreamPolicy);
     };
 
     // Two barriers per row: (1) the row and the per-wave partial sums are in

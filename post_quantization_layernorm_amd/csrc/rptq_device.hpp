@@ -13,6 +13,11 @@ namespace rptq {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Cache policy of the streaming kernels' row loads and stores: non-temporal
+// (each byte is touched once, so it should not displace reusable lines or
+// leave dirty lines behind for the next kernel to write back).
+constexpr int kStreamPolicy = 2;
+
 // Raw buffer resource over [base, base + bytes): loads past the end read as
 // zero and stores past the end are dropped (range check in hardware).
 constexpr uint32_t kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
@@ -149,9 +154,9 @@ __device__ __forceinline__ void load_row_chunks(chunk_t<VEC16> (&buf)[N], const 
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         if constexpr (VEC16)
-            buf[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(tid + i * nt) * 16u, 0, 0);
+            buf[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(tid + i * nt) * 16u, 0, kStreamPolicy);
         else
-            buf[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(tid + i * nt) * 4u, 0, 0);
+            buf[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(tid + i * nt) * 4u, 0, kStreamPolicy);
     }
 }
 
@@ -170,9 +175,9 @@ __device__ __forceinline__ void store_row_chunks(void* base, int64_t bytes, cons
     for (int i = 0; i < N; ++i) {
         const int c = tid + i * nt;
         if constexpr (VEC16)
-            __builtin_amdgcn_raw_buffer_store_b128(reinterpret_cast<const u32x4*>(lds)[c], r, (uint32_t)c * 16u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(reinterpret_cast<const u32x4*>(lds)[c], r, (uint32_t)c * 16u, 0, kStreamPolicy);
         else
-            __builtin_amdgcn_raw_buffer_store_b32(reinterpret_cast<const uint32_t*>(lds)[c], r, (uint32_t)c * 4u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(reinterpret_cast<const uint32_t*>(lds)[c], r, (uint32_t)c * 4u, 0, kStreamPolicy);
     }
 }
 
