@@ -120,13 +120,13 @@ def main():
     x = torch.from_numpy(synthetic.tokens(M, mu, sg, w.seed, synthetic.STREAM_EVAL)).to(dev)
     log(f"[bench] layer inputs ready ({time.time() - t_setup:.1f}s)")
     W = synthetic.weights(K, N, w.seed)
-    wq, s_w = P.rptq_quantize_weights(W, w.w_bits)
+    wts = {}                       # weight bits -> (packed W', colsum, s_w) on the device
+    for wb in (w.w_bits, 3):
+        wq, s_w = P.rptq_quantize_weights(W, wb)
+        wp, cs = P.rptq_pack_weights(wq, R, bounds, wb)
+        wts[wb] = (torch.from_numpy(wp).to(dev), torch.from_numpy(cs).to(dev), torch.from_numpy(s_w).to(dev))
+        del wq, wp
     del W
-    wp, cs = P.rptq_pack_weights(wq, R, bounds, w.w_bits)
-    del wq
-    wp_d = torch.from_numpy(wp).to(dev); cs_d = torch.from_numpy(cs).to(dev)
-    sw_d = torch.from_numpy(s_w).to(dev)
-    del wp
     variants = {}
     for ab in (4, 3):
         s, z = P.rptq_cluster_params(mx, mn, R, bounds, ab)
@@ -159,7 +159,7 @@ def main():
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ one step
-    names = ["ln4", "gemm4", "ln3", "gemm3", "kvq_K", "kvq_V", "kvd_K", "kvd_V"]
+    names = ["ln4", "gemm4", "ln3", "gemm3", "gemm3w3", "kvq_K", "kvq_V", "kvd_K", "kvd_V"]
 
     def step(ev=None):
         def rec(i):
@@ -171,9 +171,16 @@ def main():
             rec(k)
             P.rptq_ln_reorder_quant(x, R_d, gr_d, br_d, bounds, v["s"], v["z"], ab, out=v["codes"], stream=stream)
             rec(k + 1)
+            wp_d, cs_d, sw_d = wts[w.w_bits]
             P.rptq_qgemm(v["codes"], M, K, N, bounds, v["s"], v["z"], ab, wp_d, w.w_bits, sw_d, cs_d, out=Y,
                          stream=stream)
             k += 2
+            if ab == 3:                    # the same 3-bit codes against 3-bit weights (W3A3)
+                rec(k)
+                wp_d, cs_d, sw_d = wts[3]
+                P.rptq_qgemm(v["codes"], M, K, N, bounds, v["s"], v["z"], ab, wp_d, 3, sw_d, cs_d, out=Y,
+                             stream=stream)
+                k += 1
         rec(k)
         for name in ("K", "V"):
             d = kv[name]
@@ -255,7 +262,7 @@ def main():
         "dtype": "int8",
         "data": "synthetic (seeded per-channel N(mu_c, sigma_c) activations with 1% x100 outlier channels; "
                 "W ~ N(0, 0.02))",
-        "config": {"workload": "OPT-66B fc1 layer W4A4 (+W4A3): LayerNorm(9216)+per-cluster quant -> "
+        "config": {"workload": "OPT-66B fc1 layer W4A4 (+W4A3, W3A3): LayerNorm(9216)+per-cluster quant -> "
                                "9216x36864 GEMM, 16384 tokens, g=32; plus OPT-66B KV cache 3-bit, "
                                "2 x [524288 x 9216] fp16",
                    "M": M, "K": K, "N": N, "g": g, "K_pad": kpad, "tokens_per_step": M},
@@ -265,6 +272,9 @@ def main():
         "ln_quant_frac_hbm_peak": res_layer[4]["ln_frac_hbm_peak"],
         "w4a3": res_layer[3],
         "w4a4": res_layer[4],
+        "w3a3": {"gemm_ms": avg["gemm3w3"] * 1e3, "gemm_tops": ops / avg["gemm3w3"] / 1e12,
+                 "gemm_frac_int8_peak": ops / avg["gemm3w3"] / 1e12 / INT8_PEAK_TOPS,
+                 "tokens_per_s": M / (avg["ln3"] + avg["gemm3w3"])},
         **out,
         "per_kernel_ms": {n: avg[n] * 1e3 for n in names},
         "roofline": roofline,

@@ -131,7 +131,9 @@ int rptq_ln_reorder_quant(const void* x, int32_t in_mode, int64_t M, int32_t K,
  * bounds, s, z   host; a_bits in {3, 4, 8}.
  * w_packed device, output of rptq_pack_weights: [N][K_pad] w_bits-bit two's
  *          complement codes, K contiguous per output feature, grouped like
- *          the activation codes (w_bits in {4, 8}); pad rows are 0.
+ *          the activation codes (w_bits in {3, 4, 8}; 3-bit weights are
+ *          the W3 settings of the write-up's evaluation, W3A3KV); pad rows
+ *          are 0.
  * s_w      device fp32 [N];  colsum device int32 [g][N].
  * Y        device fp32 [M][N], row-major.
  * acc_debug device int32 [g][M][N] or NULL: receives every acc_c (validation).
@@ -222,7 +224,8 @@ int rptq_cluster_params(const float* mx, const float* mn, const int32_t* R,
  * Symmetric per-output-channel round-to-nearest weight quantization (host):
  *   s_w[n] = max_k |W[k][n]| / (2^(wb-1) - 1)   (1 for an all-zero column)
  *   wq[k][n] = clip(rne(W[k][n] / s_w[n]), -(2^(wb-1)-1), 2^(wb-1)-1)
- * W host fp32 [K][N]; wq host int8 [K][N]; s_w host fp32 [N]; w_bits in {4, 8}.
+ * W host fp32 [K][N]; wq host int8 [K][N]; s_w host fp32 [N]; w_bits in
+ * {3, 4, 8} (3 bit: codes in [-3, 3]).
  */
 int rptq_quantize_weights(const float* W, int32_t K, int32_t N, int32_t w_bits,
                           int8_t* wq, float* s_w);

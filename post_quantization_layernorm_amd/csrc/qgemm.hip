@@ -17,7 +17,7 @@
 //     2 x 2 grid of v_mfma_i32_32x32x32_i8 tiles;
 //   - K advances in stages of 128 codes (4 MFMA steps of 32).  Clusters are
 //     padded to multiples of 32 codes, so a step never straddles clusters;
-//   - A (3/4/8-bit activation codes) and W' (4/8-bit weights) are fetched
+//   - A (3/4/8-bit activation codes) and W' (3/4/8-bit weights) are fetched
 //     packed with buffer loads (scalar stage offsets; rows past M or N read
 //     as zero) about two stages ahead and staged in a double-buffered LDS
 //     tile.  W' is unpacked to int8 on the way in (row stride 144 B: the
@@ -31,9 +31,10 @@
 //     the last step of cluster c it is converted and added to fp32 out with
 //     weight d_c = s_c - s_(c+1) (summation by parts of sum_c s_c acc_c), so
 //     the accumulators are never reset and every step is the same code;
-//   - 8-bit codes q are staged as q - 128 (signed MFMA operands) and 4-bit
+//   - 8-bit codes q are staged as q - 128 (signed MFMA operands), 4-bit
 //     weights as 16 * w (nibble moved to the high half of the byte, sign for
-//     free); both are undone exactly: s_c / 16 in the scale, and
+//     free) and 3-bit weights as 32 * w; all are undone exactly: s_c / 16 or
+//     s_c / 32 in the scale, and
 //     corr[n] = sum_c s_c (z_c - offset) colsum_c[n] (fp64) in the epilogue;
 //   - workgroups are numbered so that consecutive tiles of a group land on
 //     the same XCD (the dispatcher deals workgroups round-robin over the 8
@@ -89,12 +90,24 @@ __device__ __forceinline__ void unpack_act(const uint32_t (&d)[BITS], uint32_t (
     }
 }
 
-// Weight codes (two's complement) -> 32 int8; 4-bit weights come out as 16*w.
+// Weight codes (two's complement) -> 32 int8 in natural code order; 4-bit
+// weights come out as 16*w and 3-bit weights as 32*w (the field moved to
+// the top of its byte, so the byte's sign is the weight's).
 template <int BITS>
 __device__ __forceinline__ void unpack_wgt(const uint32_t (&d)[BITS], uint32_t (&o)[8]) {
     if constexpr (BITS == 8) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] = d[i];
+    } else if constexpr (BITS == 3) {
+        // byte j of words d0, d1, d2 holds codes j, j+4 | j+8, j+12 | j+16,
+        // j+20 in bits 0-2 / 3-5; codes j+24 and j+28 keep their low two bits
+        // in bits 6-7 of d0 and d1 and their top bit in bits 6 and 7 of d2
+        const uint32_t m = 0xE0E0E0E0u;
+        o[0] = (d[0] << 5) & m;  o[1] = (d[0] << 2) & m;
+        o[2] = (d[1] << 5) & m;  o[3] = (d[1] << 2) & m;
+        o[4] = (d[2] << 5) & m;  o[5] = (d[2] << 2) & m;
+        o[6] = ((d[0] >> 1) & 0x60606060u) | ((d[2] << 1) & 0x80808080u);
+        o[7] = ((d[1] >> 1) & 0x60606060u) | (d[2] & 0x80808080u);
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -277,7 +290,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
                         const int64_t m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
                         const int v = acc[i][j][r] - prev[i][j][r];
                         if (m < M && n < N)
-                            acc_dbg[((int64_t)cl * M + m) * N + n] = (WBITS == 4 ? (v >> 4) : v) + add;
+                            acc_dbg[((int64_t)cl * M + m) * N + n] = (WBITS == 4 ? (v >> 4) : WBITS == 3 ? (v >> 5) : v) + add;
                     }
                     prev[i][j] = acc[i][j];
                 }
@@ -404,7 +417,7 @@ const void* pick2(bool debug) {
 
 template <int ABITS>
 const void* pick(int wbits, bool debug) {
-    return wbits == 4 ? pick2<ABITS, 4>(debug) : pick2<ABITS, 8>(debug);
+    return wbits == 3 ? pick2<ABITS, 3>(debug) : wbits == 4 ? pick2<ABITS, 4>(debug) : pick2<ABITS, 8>(debug);
 }
 
 }  // namespace

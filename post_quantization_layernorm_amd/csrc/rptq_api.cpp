@@ -42,6 +42,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 bool valid_bits(int32_t b) { return b == 3 || b == 4 || b == 8; }
 
+// weight bits: 3 and 4 (packed) or 8
+bool valid_wbits(int32_t b) { return b == 3 || b == 4 || b == 8; }
+
 // bounds: host int32[g+1], 1 <= g <= min(K, 64), 0 = b0 < b1 < ... < bg = K.
 int check_bounds(const int32_t* bounds, int32_t g, int32_t K) {
     if (!bounds) return fail(RPTQ_ERR_INVALID_ARG, "bounds is NULL");
@@ -151,7 +154,7 @@ int64_t rptq_codes_row_bytes(const int32_t* bounds, int32_t g, int32_t bits) {
 }
 
 int64_t rptq_weights_row_bytes(const int32_t* bounds, int32_t g, int32_t w_bits) {
-    if ((w_bits != 4 && w_bits != 8) || check_bounds(bounds, g, -1) != RPTQ_OK) return -1;
+    if (!valid_wbits(w_bits) || check_bounds(bounds, g, -1) != RPTQ_OK) return -1;
     return (int64_t)kpad_of(bounds, g) * w_bits / 8;
 }
 
@@ -198,7 +201,7 @@ int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N, const int3
     if (M < 0) return fail(RPTQ_ERR_INVALID_ARG, "M = %lld < 0", (long long)M);
     if (K < 1 || N < 1) return fail(RPTQ_ERR_INVALID_ARG, "K = %d, N = %d must be >= 1", K, N);
     if (!valid_bits(a_bits)) return fail(RPTQ_ERR_INVALID_ARG, "a_bits = %d not in {3, 4, 8}", a_bits);
-    if (w_bits != 4 && w_bits != 8) return fail(RPTQ_ERR_INVALID_ARG, "w_bits = %d not in {4, 8}", w_bits);
+    if (!valid_wbits(w_bits)) return fail(RPTQ_ERR_INVALID_ARG, "w_bits = %d not in {3, 4, 8}", w_bits);
     int st = check_bounds(bounds, g, K);
     if (st) return st;
     if ((st = check_params(s, z, g))) return st;
@@ -220,10 +223,11 @@ int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N, const int3
         ga.sz[c] = (double)s[c] * ((double)z[c] - (double)ga.code_offset);
     }
     // flush weights of the running accumulator: d_c = s_c - s_(c+1), s_(g+1) = 0
-    // (4-bit weights are staged as 16 * w, hence the 1/16)
+    // (4-bit weights are staged as 16 * w and 3-bit weights as 32 * w, hence
+    // the 1/16 and 1/32)
     for (int c = 0; c < g; ++c) {
         const double d = (double)s[c] - (c + 1 < g ? (double)s[c + 1] : 0.0);
-        ga.scale[c] = (float)(w_bits == 4 ? d * 0.0625 : d);
+        ga.scale[c] = (float)(w_bits == 4 ? d * 0.0625 : w_bits == 3 ? d * 0.03125 : d);
     }
     ga.nsteps = steps;
     const int64_t a_row_bytes = (int64_t)steps * 32 * a_bits / 8;
@@ -431,7 +435,7 @@ int rptq_cluster_params(const float* mx, const float* mn, const int32_t* R, cons
 int rptq_quantize_weights(const float* W, int32_t K, int32_t N, int32_t w_bits, int8_t* wq, float* s_w) {
     if (!W || !wq || !s_w) return fail(RPTQ_ERR_INVALID_ARG, "NULL argument");
     if (K < 1 || N < 1) return fail(RPTQ_ERR_INVALID_ARG, "K = %d, N = %d", K, N);
-    if (w_bits != 4 && w_bits != 8) return fail(RPTQ_ERR_INVALID_ARG, "w_bits = %d", w_bits);
+    if (!valid_wbits(w_bits)) return fail(RPTQ_ERR_INVALID_ARG, "w_bits = %d", w_bits);
     const int qm = (1 << (w_bits - 1)) - 1;
     std::vector<double> amax(N, 0.0);
     for (int64_t k = 0; k < K; ++k)
@@ -459,7 +463,7 @@ int rptq_pack_weights(const int8_t* wq, int32_t K, int32_t N, int32_t w_bits, co
                       const int32_t* bounds, int32_t g, uint8_t* w_packed, int32_t* colsum) {
     if (!wq || !w_packed || !colsum) return fail(RPTQ_ERR_INVALID_ARG, "NULL argument");
     if (K < 1 || N < 1) return fail(RPTQ_ERR_INVALID_ARG, "K = %d, N = %d", K, N);
-    if (w_bits != 4 && w_bits != 8) return fail(RPTQ_ERR_INVALID_ARG, "w_bits = %d", w_bits);
+    if (!valid_wbits(w_bits)) return fail(RPTQ_ERR_INVALID_ARG, "w_bits = %d", w_bits);
     int st = check_bounds(bounds, g, K);
     if (st) return st;
     const int qm = (1 << (w_bits - 1)) - 1;
@@ -497,6 +501,19 @@ int rptq_pack_weights(const int8_t* wq, int32_t K, int32_t N, int32_t w_bits, co
                 uint8_t* dst = w_packed + (int64_t)n * rb;
                 if (w_bits == 8) {
                     for (int32_t p = 0; p < kp; ++p) dst[p] = (uint8_t)col[p];
+                } else if (w_bits == 3) {
+                    // 32 weights -> 12 bytes, the activation codes' 3-bit group
+                    // layout on the 3-bit two's complement fields
+                    for (int32_t p = 0; p < kp; p += 32) {
+                        uint8_t* gb = dst + p / 32 * 12;
+                        for (int j = 0; j < 4; ++j) {
+                            int f[8];
+                            for (int e = 0; e < 8; ++e) f[e] = col[p + j + 4 * e] & 7;
+                            gb[j] = (uint8_t)(f[0] | f[1] << 3 | (f[6] & 3) << 6);
+                            gb[4 + j] = (uint8_t)(f[2] | f[3] << 3 | (f[7] & 3) << 6);
+                            gb[8 + j] = (uint8_t)(f[4] | f[5] << 3 | (f[6] >> 2) << 6 | (f[7] >> 2) << 7);
+                        }
+                    }
                 } else {
                     for (int32_t p = 0; p < kp; p += 8)
                         for (int i = 0; i < 4; ++i)

@@ -101,7 +101,7 @@ def _gemm(P, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(a_bits=2), -1), (dict(w_bits=3), -1), (dict(w_bits=16), -1), (dict(N=0), -1), (dict(M=-3), -1),
+    (dict(a_bits=2), -1), (dict(w_bits=2), -1), (dict(w_bits=16), -1), (dict(N=0), -1), (dict(M=-3), -1),
     (dict(K=63), -1), (dict(s=np.array([0.1, -0.2], np.float32)), -1), (dict(w=None), -1),
     (dict(colsum=None), -1), (dict(Y=None), -1), (dict(s_w=None), -1),
     (dict(K=16392, bounds=np.array([0, 8, 16392], np.int32)), -2),
@@ -173,13 +173,13 @@ def test_host_kmeans_reorder_matches_oracle(P, orc):
 def test_host_weight_quantization_matches_oracle(P, orc):
     W = synthetic.weights(96, 40, 5)
     W[:, 3] = 0
-    for wb in (4, 8):
+    for wb in (3, 4, 8):
         wq_o, sw_o = orc.quantize_weights(W, wb)
         wq_p, sw_p = P.rptq_quantize_weights(W, wb)
         assert np.array_equal(wq_o, wq_p) and np.array_equal(sw_o, sw_p)
 
 
-@pytest.mark.parametrize("wb", [4, 8])
+@pytest.mark.parametrize("wb", [3, 4, 8])
 def test_host_pack_weights_reorders_pads_and_sums(P, orc, wb):
     r = np.random.default_rng(wb)
     K, N = 100, 24
@@ -193,10 +193,8 @@ def test_host_pack_weights_reorders_pads_and_sums(P, orc, wb):
     # the packed rows use the same group layout as activation codes (two's
     # complement nibbles); decode with the oracle's unpacker
     codes = orc.unpack_dense(wp, kp, wb).astype(np.int16)
-    if wb == 4:
-        codes = np.where(codes >= 8, codes - 16, codes)
-    else:
-        codes = np.where(codes >= 128, codes - 256, codes)
+    half = 2 ** (wb - 1)
+    codes = np.where(codes >= half, codes - 2 * half, codes)
     dense, pad = orc.unpack_seg32(orc.pack_dense(np.zeros((N, kp), np.uint8), 8), K, bounds, 8, return_pad=True)
     # rebuild reordered weights from the padded sequence
     off = 0

@@ -1,6 +1,6 @@
 """GPU parity at the full benchmark sizes, in the launch configurations the
 benchmark times: the OPT-66B fc1 layer (16384 tokens x 9216 -> 36864, g = 32,
-W4A4 and W4A3) and the OPT-66B K/V cache (524288 tokens x 9216 channels,
+W4A4, W4A3 and W3A3) and the OPT-66B K/V cache (524288 tokens x 9216 channels,
 3 bit).  The device runs every row; the oracle checks sampled rows one by one
 (its cost grows with the sample, not with the launch).  All parameters (R,
 bounds, s, z, Wq) come from the oracle's calibration."""
@@ -41,13 +41,15 @@ def fc1():
     xc = synthetic.tokens(w.calib_tokens, mu, sg, w.seed, synthetic.STREAM_CALIB)
     mx, mn = orc.channel_minmax(orc.layernorm(xc, gamma, beta))
     x = synthetic.tokens(M, mu, sg, w.seed, synthetic.STREAM_EVAL)
-    Wq, s_w = orc.quantize_weights(synthetic.weights(K, N, w.seed), w.w_bits)
+    W = synthetic.weights(K, N, w.seed)
+    wq = {wb: orc.quantize_weights(W, wb) for wb in (w.w_bits, 3)}
+    del W
     u = synthetic.kmeans_uniforms(w.seed, 3, g)
     params = {}
     for ab in (4, 3):
         params[ab] = orc.calibrate(mx, mn, g, ab, u, n_init=3)
     _say("calibrated")
-    return dict(M=M, K=K, N=N, g=g, x=x, gamma=gamma, beta=beta, Wq=Wq, s_w=s_w, params=params)
+    return dict(M=M, K=K, N=N, g=g, x=x, gamma=gamma, beta=beta, wq=wq, params=params)
 
 
 ROWS = np.array([0, 1, 255, 256, 4097, 9000, 16382, 16383])
@@ -69,21 +71,22 @@ def test_fc1_fullsize_ln_quant_sampled(P, fc1, ab):
     assert d.max() <= 1 and (d > 0).mean() <= 1e-3, (d.max(), (d > 0).mean())
 
 
-@pytest.mark.parametrize("ab", [4, 3])
-def test_fc1_fullsize_gemm_sampled(P, fc1, ab):
+@pytest.mark.parametrize("ab,wb", [(4, 4), (3, 4), (3, 3)])
+def test_fc1_fullsize_gemm_sampled(P, fc1, ab, wb):
     M, K, N, g = fc1["M"], fc1["K"], fc1["N"], fc1["g"]
     R, bounds, s, z = fc1["params"][ab]
-    _say("gemm", ab)
+    Wq, s_w = fc1["wq"][wb]
+    _say("gemm", ab, wb)
     # every row's codes from the oracle, so Y isolates the GEMM
     codes_o = orc.ln_reorder_quant(fc1["x"], fc1["gamma"], fc1["beta"], 1e-5, R, bounds, s, z, ab)
-    wp, cs = P.rptq_pack_weights(fc1["Wq"], R, bounds, 4)
-    wp, cs, sw = dev(wp), dev(cs), dev(fc1["s_w"])
+    wp, cs = P.rptq_pack_weights(Wq, R, bounds, wb)
+    wp, cs, sw = dev(wp), dev(cs), dev(s_w)
     cd = dev(codes_o)
-    Y = P.rptq_qgemm(cd, M, K, N, bounds, s, z, ab, wp, 4, sw, cs)
+    Y = P.rptq_qgemm(cd, M, K, N, bounds, s, z, ab, wp, wb, sw, cs)
     Ys = Y[torch.from_numpy(ROWS).cuda()].cpu().numpy()
     del Y
     q = orc.unpack_seg32(codes_o[ROWS], K, bounds, ab)
-    Y_o, acc_o = orc.qgemm(q, fc1["Wq"], R, bounds, s, z, fc1["s_w"], return_acc=True)
+    Y_o, acc_o = orc.qgemm(q, Wq, R, bounds, s, z, s_w, return_acc=True)
     assert rel_l2(Ys, Y_o) <= 1e-3
     for i in range(len(ROWS)):
         assert rel_l2(Ys[i], Y_o[i]) <= 1e-3, i
@@ -91,9 +94,9 @@ def test_fc1_fullsize_gemm_sampled(P, fc1, ab):
     # full-size debug buffer would be g x M x N x 4 bytes)
     r0 = 4096
     acc = torch.zeros((g, 64, N), dtype=torch.int32, device="cuda")
-    P.rptq_qgemm(cd[r0:r0 + 64], 64, K, N, bounds, s, z, ab, wp, 4, sw, cs, acc_debug=acc)
+    P.rptq_qgemm(cd[r0:r0 + 64], 64, K, N, bounds, s, z, ab, wp, wb, sw, cs, acc_debug=acc)
     q64 = orc.unpack_seg32(codes_o[r0:r0 + 64], K, bounds, ab)
-    _, acc64 = orc.qgemm(q64, fc1["Wq"], R, bounds, s, z, fc1["s_w"], return_acc=True)
+    _, acc64 = orc.qgemm(q64, Wq, R, bounds, s, z, s_w, return_acc=True)
     assert np.array_equal(acc.cpu().numpy(), acc64)
 
 

@@ -175,6 +175,9 @@ GEMM_CASES = [  # (M, K, N, g, a_bits, w_bits)
     (64, 9216, 136, 32, 3, 4),          # OPT-66B-shaped W4A3
     (33, 9216, 128, 32, 4, 4),
     (1, 512, 72, 4, 4, 8),              # M = 1
+    (64, 9216, 136, 32, 3, 3),          # OPT-66B-shaped W3A3 (the write-up's W3A3KV setting)
+    (70, 2048, 392, 8, 4, 3),           # W3A4, ragged M and N
+    (40, 768, 200, 4, 8, 3),            # W3A8
 ]
 
 
@@ -199,7 +202,7 @@ def test_qgemm_accumulators_bit_exact_and_y(P, case):
 @pytest.mark.parametrize("bounds", [[0, 1, 2, 3, 64, 96, 97, 160, 256], [0, 256],
                                     list(range(0, 65)) + [256]],
                          ids=["size1", "g1", "g65"])
-@pytest.mark.parametrize("ab,wb", [(3, 4), (4, 4), (8, 8), (8, 4)])
+@pytest.mark.parametrize("ab,wb", [(3, 4), (4, 4), (8, 8), (8, 4), (3, 3), (8, 3)])
 def test_qgemm_ragged_clusters(P, bounds, ab, wb):
     if len(bounds) - 1 > 64:
         bounds = bounds[:64] + [256]                  # g = 64: 63 singletons + one big cluster
@@ -213,16 +216,16 @@ def test_qgemm_ragged_clusters(P, bounds, ab, wb):
     assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
 
 
-@pytest.mark.parametrize("ab", [3, 4, 8])
-def test_end_to_end_ln_then_gemm(P, ab):
+@pytest.mark.parametrize("ab,wb", [(3, 4), (4, 4), (8, 4), (3, 3)])
+def test_end_to_end_ln_then_gemm(P, ab, wb):
     M, K, N, g = 150, 2048, 520, 8
-    c = layer_case(M, K, N, g, ab, 4, seed=77 + ab)
+    c = layer_case(M, K, N, g, ab, wb, seed=77 + ab)
     _, codes_o = _oracle_codes(c)
     q = orc.unpack_seg32(codes_o, K, c.bounds, ab)
     Y_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w)
     codes = _fused(P, c, ab)
     wp, cs, sw = _gemm_inputs(P, c)
-    Y = P.rptq_qgemm(codes, M, K, N, c.bounds, c.s, c.z, ab, wp, 4, sw, cs)
+    Y = P.rptq_qgemm(codes, M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs)
     assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
 
 

@@ -419,7 +419,7 @@ def test_qgemm_matches_dequantized_matmul_realistic(orc):
     np.testing.assert_allclose(Y.astype(np.float64), ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
 
 
-@pytest.mark.parametrize("wbits", [4, 8])
+@pytest.mark.parametrize("wbits", [3, 4, 8])
 def test_weight_quantization_bounds(orc, wbits):
     W = synthetic.weights(64, 40, 3)
     W[:, 7] = 0.0
