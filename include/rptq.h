@@ -145,6 +145,44 @@ int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N,
                const uint8_t* w_packed, int32_t w_bits, const float* s_w, const int32_t* colsum,
                float* Y, int32_t* acc_debug, void* stream);
 
+/* Activation applied to Y before the quantized output of rptq_qgemm_quant. */
+enum {
+    RPTQ_ACT_NONE = 0,
+    RPTQ_ACT_RELU = 1             /* max(y, 0): OPT's fc1 -> fc2 */
+};
+
+/*
+ * The same GEMM, with its output quantized for the next layer in the
+ * epilogue (RPTQ write-up, method and Fig. 3: the weights of a linear layer
+ * are reordered so that the layer produces its activations directly in the
+ * sorted (reordered) order of the layer that consumes them; this is how the
+ * inputs that no LayerNorm produces -- e.g. fc2's, after fc1 and the
+ * activation -- reach the next GEMM as per-cluster codes without an explicit
+ * reorder).
+ *   y[m][p]        = act(Y[m][p])   for the output features in the next
+ *                    layer's reordered SEG32 positions p
+ *   out_codes[m]   = SEG32 pack of q = clip(rne(y * (1/s_c)) + z_c, 0, qmax)
+ *                    with c the next layer's cluster of p; pad codes 0
+ * which is exactly rptq_ln_reorder_quant's quantization (mode 1) applied to
+ * the fp32 y.
+ * N_pad    the next layer's K_pad (rptq_codes_kpad(out_bounds, out_g)): the
+ *          GEMM's output features are the padded positions, so w_packed,
+ *          s_w and colsum come from rptq_pack_weights_out (pad features have
+ *          zero weights).
+ * act      RPTQ_ACT_NONE or RPTQ_ACT_RELU.
+ * out_bounds, out_s, out_z, out_bits   host: the next layer's clusters (its
+ *          R is folded into the weight layout); out_bits in {3, 4, 8}.
+ * out_codes device [M][rptq_codes_row_bytes(out_bounds, out_g, out_bits)].
+ * Y        device fp32 [M][N_pad] or NULL: also receives y (after the
+ *          activation; pad columns 0), for validation.
+ * Other arguments, limits and errors as rptq_qgemm.
+ */
+int rptq_qgemm_quant(const uint8_t* codes, int64_t M, int32_t K, int32_t N_pad,
+                     const int32_t* bounds, int32_t g, const float* s, const int32_t* z, int32_t a_bits,
+                     const uint8_t* w_packed, int32_t w_bits, const float* s_w, const int32_t* colsum,
+                     int32_t act, const int32_t* out_bounds, int32_t out_g, const float* out_s,
+                     const int32_t* out_z, int32_t out_bits, uint8_t* out_codes, float* Y, void* stream);
+
 /*
  * K/V-cache quantize + pack (RPTQ write-up, evaluation: the KV-cache settings
  * W4A4KV / W4A3KV / W3A3KV quantize the key and value caches, which hold most
@@ -243,6 +281,22 @@ int rptq_quantize_weights(const float* W, int32_t K, int32_t N, int32_t w_bits,
 int rptq_pack_weights(const int8_t* wq, int32_t K, int32_t N, int32_t w_bits,
                       const int32_t* R, const int32_t* bounds, int32_t g,
                       uint8_t* w_packed, int32_t* colsum);
+
+/*
+ * rptq_pack_weights for a layer whose output feeds rptq_qgemm_quant (host):
+ * the output features are put in the next layer's reordered order R_out and
+ * SEG32-padded by out_bounds (pad features: zero weights, colsum 0, s_w 1),
+ * so that output feature p of the packed layer is the next layer's padded
+ * position p.
+ * s_w host fp32 [N] natural order (from rptq_quantize_weights);
+ * w_packed host uint8 [N_pad][rptq_weights_row_bytes(bounds, g, w_bits)];
+ * colsum host int32 [g][N_pad]; s_w_out host fp32 [N_pad];
+ * N_pad = rptq_codes_kpad(out_bounds, out_g); R_out host int32 [N] or NULL.
+ */
+int rptq_pack_weights_out(const int8_t* wq, int32_t K, int32_t N, int32_t w_bits,
+                          const int32_t* R, const int32_t* bounds, int32_t g,
+                          const int32_t* R_out, const int32_t* out_bounds, int32_t out_g,
+                          const float* s_w, uint8_t* w_packed, int32_t* colsum, float* s_w_out);
 
 /* ---------------------------------------------------------- sizes, errors */
 

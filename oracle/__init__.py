@@ -290,6 +290,23 @@ def qgemm(q, Wq, R, bounds, s, z, s_w, return_acc=False):
     return (Y, acc) if return_acc else Y
 
 
+def qgemm_quant(q, Wq, R, bounds, s, z, s_w, act, R_out, out_bounds, out_s, out_z, out_bits, return_y=False):
+    """A linear layer whose weights are reordered so that it produces its
+    output directly in the next layer's sorted order (RPTQ write-up, method
+    and Fig. 3), quantized per next-layer cluster and packed (SEG32):
+      Y      = qgemm(...)                        fp32 [M][N], natural order
+      y[:,j] = act(Y[:, R_out[j]])               act 0: identity, 1: max(., 0)
+      codes  = pack_seg32(quantize(y, out_bounds, out_s, out_z, out_bits))
+    The steps are the oracle's own GEMM, quantizer and packer, in this order."""
+    Y = qgemm(q, Wq, R, bounds, s, z, s_w)
+    if act:
+        Y = np.maximum(Y, np.float32(0.0))
+    y = Y if R_out is None else Y[:, np.asarray(R_out)]
+    y = np.ascontiguousarray(y, np.float32)
+    codes = pack_seg32(quantize(y, out_bounds, out_s, out_z, out_bits), out_bounds, out_bits)
+    return (codes, y) if return_y else codes
+
+
 # ----------------------------------------------------------------------------- KV cache
 def kv_quant_pack(kv_f16, R, bounds, s, z, bits) -> np.ndarray:
     kv = _c(np.asarray(kv_f16).view(np.uint16), np.uint16); T, C = kv.shape

@@ -29,13 +29,15 @@ RPTQ_ERR_HIP = -4
 RPTQ_IN_FP16_RAW = 0
 RPTQ_IN_FP32_NORMALIZED = 1
 RPTQ_CALIB_RAW = 2
+RPTQ_ACT_NONE = 0
+RPTQ_ACT_RELU = 1
 RPTQ_MAX_CLUSTERS = 64
 RPTQ_MAX_K = 16384
 
 EXPORTED = [
-    "rptq_ln_reorder_quant", "rptq_qgemm", "rptq_kv_quant_pack", "rptq_kv_dequant",
+    "rptq_ln_reorder_quant", "rptq_qgemm", "rptq_qgemm_quant", "rptq_kv_quant_pack", "rptq_kv_dequant",
     "rptq_calib_minmax", "rptq_kmeans_reorder", "rptq_cluster_params", "rptq_quantize_weights",
-    "rptq_pack_weights", "rptq_codes_kpad", "rptq_codes_row_bytes", "rptq_weights_row_bytes",
+    "rptq_pack_weights", "rptq_pack_weights_out", "rptq_codes_kpad", "rptq_codes_row_bytes", "rptq_weights_row_bytes",
     "rptq_kv_row_bytes", "rptq_status_string", "rptq_last_error", "rptq_version",
 ]
 
@@ -69,6 +71,8 @@ def lib() -> ctypes.CDLL:
             "rptq_ln_reorder_quant": (_I32, [_P, _I32, _I64, _I32, _P, _P, ctypes.c_float, _P, _P, _I32,
                                              _P, _P, _I32, _P, _P]),
             "rptq_qgemm": (_I32, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
+            "rptq_qgemm_quant": (_I32, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _I32,
+                                        _P, _I32, _P, _P, _I32, _P, _P, _P]),
             "rptq_kv_quant_pack": (_I32, [_P, _I64, _I32, _P, _P, _I32, _P, _P, _I32, _P, _P]),
             "rptq_kv_dequant": (_I32, [_P, _I64, _I32, _P, _P, _I32, _P, _P, _I32, _P, _P]),
             "rptq_calib_minmax": (_I32, [_P, _I32, _I64, _I32, _P, _P, ctypes.c_float, _P, _P, _P]),
@@ -76,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "rptq_cluster_params": (_I32, [_P, _P, _P, _P, _I32, _I32, _P, _P]),
             "rptq_quantize_weights": (_I32, [_P, _I32, _I32, _I32, _P, _P]),
             "rptq_pack_weights": (_I32, [_P, _I32, _I32, _I32, _P, _P, _I32, _P, _P]),
+            "rptq_pack_weights_out": (_I32, [_P, _I32, _I32, _I32, _P, _P, _I32, _P, _P, _I32, _P, _P, _P, _P]),
             "rptq_codes_kpad": (_I32, [_P, _I32]),
             "rptq_codes_row_bytes": (_I64, [_P, _I32, _I32]),
             "rptq_weights_row_bytes": (_I64, [_P, _I32, _I32]),
@@ -180,6 +185,26 @@ def rptq_qgemm(codes, M, K, N, bounds, s, z, a_bits, w_packed, w_bits, s_w, cols
     return out
 
 
+def rptq_qgemm_quant(codes, M, K, N_pad, bounds, s, z, a_bits, w_packed, w_bits, s_w, colsum, act,
+                     out_bounds, out_s, out_z, out_bits, out=None, y_out=None, stream=None):
+    """The GEMM with its output quantized for the next layer.  w_packed, s_w,
+    colsum: cuda, from rptq_pack_weights_out.  Returns cuda uint8 SEG32 codes
+    [M][rptq_codes_row_bytes(out_bounds, out_bits)]; y_out (optional cuda fp32
+    [M][N_pad]) receives the activated output before quantization."""
+    b = _h(bounds, np.int32); sh = _h(s, np.float32); zh = _h(z, np.int32)
+    ob = _h(out_bounds, np.int32); osh = _h(out_s, np.float32); ozh = _h(out_z, np.int32)
+    if out is None:
+        rb = rptq_codes_row_bytes(ob, out_bits)
+        if rb < 0:
+            _check(RPTQ_ERR_INVALID_ARG, "rptq_codes_row_bytes")
+        out = torch.empty((M, rb), dtype=torch.uint8, device=codes.device)
+    st = lib().rptq_qgemm_quant(_dp(codes), M, K, N_pad, _hp(b), b.size - 1, _hp(sh), _hp(zh), a_bits,
+                                _dp(w_packed), w_bits, _dp(s_w), _dp(colsum), act, _hp(ob), ob.size - 1,
+                                _hp(osh), _hp(ozh), out_bits, _dp(out), _dp(y_out), _stream(stream))
+    _check(st, "rptq_qgemm_quant")
+    return out
+
+
 def rptq_kv_quant_pack(kv, R, bounds, s, z, bits, out=None, stream=None):
     """kv: cuda fp16 [T][C] natural order.  Returns cuda uint8 [T][C*bits/8]."""
     T, C = kv.shape
@@ -264,3 +289,25 @@ def rptq_pack_weights(wq, R, bounds, w_bits):
     _check(lib().rptq_pack_weights(_hp(wqh), K, N, w_bits, _hp(Rh), _hp(b), g, _hp(wp), _hp(cs)),
            "rptq_pack_weights")
     return wp, cs
+
+
+def rptq_pack_weights_out(wq, R, bounds, w_bits, R_out, out_bounds, s_w):
+    """Host.  Returns (w_packed uint8 [N_pad][K_pad*w_bits/8], colsum int32
+    [g][N_pad], s_w_out fp32 [N_pad]) with the output features in the next
+    layer's padded order."""
+    wqh = _h(wq, np.int8)
+    K, N = wqh.shape
+    Rh = None if R is None else _h(R, np.int32)
+    Roh = None if R_out is None else _h(R_out, np.int32)
+    b = _h(bounds, np.int32); g = b.size - 1
+    ob = _h(out_bounds, np.int32)
+    swh = _h(s_w, np.float32)
+    rb = rptq_weights_row_bytes(b, w_bits)
+    npad = rptq_codes_kpad(ob)
+    if rb < 0 or npad < 0:
+        _check(RPTQ_ERR_INVALID_ARG, "rptq_pack_weights_out sizes")
+    wp = np.empty((npad, rb), np.uint8); cs = np.empty((g, npad), np.int32); swo = np.empty(npad, np.float32)
+    _check(lib().rptq_pack_weights_out(_hp(wqh), K, N, w_bits, _hp(Rh), _hp(b), g, _hp(Roh), _hp(ob),
+                                       ob.size - 1, _hp(swh), _hp(wp), _hp(cs), _hp(swo)),
+           "rptq_pack_weights_out")
+    return wp, cs, swo

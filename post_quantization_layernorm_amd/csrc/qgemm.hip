@@ -145,7 +145,8 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     const uint8_t* __restrict__ A, int64_t M, int32_t a_row_bytes,
     const uint8_t* __restrict__ B, int32_t N, int32_t b_row_bytes,
     const GemmArgs ga, const float* __restrict__ s_w, const int32_t* __restrict__ colsum,
-    float* __restrict__ Y, int32_t* __restrict__ acc_dbg, int32_t tiles_m, int32_t tiles_n) {
+    float* __restrict__ Y, int32_t* __restrict__ acc_dbg, int32_t tiles_m, int32_t tiles_n,
+    const QuantOutArgs qo, const ClusterArgs qc) {
     constexpr int BM = CFG::BM, BN = CFG::BN, SK = CFG::SK, LDSS = CFG::LDSS, NT = CFG::NT;
     constexpr int PA = CFG::PA, PB = CFG::PB, WN = CFG::WN;
     constexpr int NPIECE = PA + PB;
@@ -180,9 +181,11 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     // no scalar memory loads (and their waits) inside the K loop.  The two
     // vector loads complete here, before any prefetch is issued, so the
     // memory-counter waits inside the loop never have to cover them.
-    const int lane_c = lane < ga.g ? lane : ga.g - 1;
-    const int end_l = ga.step_end[lane_c];
-    const float d_l = ga.scale[lane_c];
+    // (lanes past g hold an end that is never reached, so the loop needs no
+    // cluster count: a scalar load of it would be pending in the loop and
+    // turn the waits there into waits for every LDS read)
+    const int end_l = lane < ga.g ? ga.step_end[lane] : 0x7fffffff;
+    const float d_l = lane < ga.g ? ga.scale[lane] : 0.0f;
     asm volatile("" ::"v"(end_l), "v"(d_l) : "memory");
 
     // ---- staging: piece p = tid + i * NT covers row p / SK, step p % SK of a stage
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
         if (steps_done == c_end) {
             flush(c);
             ++c;
-            c_end = c < ga.g ? __builtin_amdgcn_readlane(end_l, c) : 0x7fffffff;
+            c_end = __builtin_amdgcn_readlane(end_l, c & 63);
         }
     };
 
@@ -391,6 +394,16 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     }
 
     // ---- epilogue: Y = s_w * (out - corr), corr[n] = sum_c s_c (z_c - offset) colsum_c[n]
+    // With a quantized output (the next layer's input, RPTQ write-up, method
+    // and Fig. 3: the layer's weights are reordered so that it produces its
+    // activations already in the next layer's sorted order), column n is the
+    // next layer's SEG32 position n: Y (after ReLU when asked) is quantized
+    // with that position's cluster (s, z) like every other activation, pad
+    // positions get code 0, and the 128 x 128 code tile is packed through LDS.
+    const bool quant = qo.q_codes != nullptr;
+    uint8_t* ctile = reinterpret_cast<uint8_t*>(&As[0][0]);     // 128 x 128 codes
+    if (quant) __syncthreads();                                 // every wave is done with the staging tiles
+    const float qhi = kRoundMagic + (float)((1 << qc.bits) - 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int n = n0 + wn * 64 + j * 32 + col_l;
@@ -398,13 +411,64 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
         double corr = 0.0;
         for (int cc = 0; cc < ga.g; ++cc) corr += ga.sz[cc] * (double)colsum[(int64_t)cc * N + n];
         const double sw = (double)s_w[n];
+        // the next layer's cluster of position n (pad positions: no cluster)
+        float inv = 0.0f, zf = 0.0f;
+        bool real = false;
+        if (quant)
+            for (int cc = 0; cc < qc.g; ++cc)
+                if (n >= qc.off[cc]) {
+                    real = n - qc.off[cc] < qc.bounds[cc + 1] - qc.bounds[cc];
+                    inv = qc.inv_s[cc];
+                    zf = (float)qc.z[cc];
+                }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
-                if (m < M) __builtin_nontemporal_store((float)(sw * ((double)out[i][j][r] - corr)), Y + m * N + n);
+                const int rl = wm * 64 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+                const int64_t m = m0 + rl;
+                float y = (float)(sw * ((double)out[i][j][r] - corr));
+                if (quant) {
+                    if (qo.act) y = __builtin_fmaxf(y, 0.0f);
+                    const uint32_t qb = quant_bits(y, inv, zf, qhi);
+                    ctile[rl * 128 + wn * 64 + j * 32 + col_l] = real ? (uint8_t)qb : 0;
+                }
+                if (Y && m < M) __builtin_nontemporal_store(y, Y + m * N + n);
             }
+    }
+    if (quant) {
+        __syncthreads();
+        // 128 rows x 4 groups of 32 positions: two groups per thread
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int gi = tid * 2 + k, rl = gi >> 2, grp = gi & 3;
+            const int64_t m = m0 + rl;
+            if (m >= M || n0 + grp * 32 >= N) continue;
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(ctile + rl * 128 + grp * 32);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(ctile + rl * 128 + grp * 32 + 16);
+            const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};   // byte = code
+            uint8_t* dst = qo.q_codes + m * qo.q_row_bytes + (int64_t)((n0 >> 5) + grp) * 4 * qc.bits;
+            if (qc.bits == 8) {
+                reinterpret_cast<u32x4*>(dst)[0] = lo;
+                reinterpret_cast<u32x4*>(dst)[1] = hi;
+            } else if (qc.bits == 4) {
+                // unit u = codes 8u .. 8u+7: byte i holds code 8u+i and, in
+                // its high nibble, code 8u+4+i
+                *reinterpret_cast<u32x4*>(dst) =
+                    u32x4{w[0] | w[1] << 4, w[2] | w[3] << 4, w[4] | w[5] << 4, w[6] | w[7] << 4};
+            } else {
+                // byte j of words d0, d1, d2: codes j, j+4 | j+8, j+12 | j+16,
+                // j+20 in bits 0-2 / 3-5; codes j+24, j+28: low two bits in bits
+                // 6-7 of d0 / d1, top bit in bit 6 / 7 of d2
+                const uint32_t d0 = w[0] | w[1] << 3 | (w[6] & 0x03030303u) << 6;
+                const uint32_t d1 = w[2] | w[3] << 3 | (w[7] & 0x03030303u) << 6;
+                const uint32_t d2 = w[4] | w[5] << 3 | ((w[6] >> 2) & 0x01010101u) << 6 |
+                                    ((w[7] >> 2) & 0x01010101u) << 7;
+                reinterpret_cast<uint32_t*>(dst)[0] = d0;
+                reinterpret_cast<uint32_t*>(dst)[1] = d1;
+                reinterpret_cast<uint32_t*>(dst)[2] = d2;
+            }
+        }
     }
 }
 
@@ -425,7 +489,8 @@ const void* pick(int wbits, bool debug) {
 hipError_t launch_qgemm(const uint8_t* codes, int64_t M, int32_t N, int64_t a_row_bytes,
                         int a_bits, const uint8_t* w_packed, int64_t w_row_bytes, int w_bits,
                         const GemmArgs& ga, const float* s_w, const int32_t* colsum,
-                        float* Y, int32_t* acc_debug, hipStream_t stream) {
+                        float* Y, int32_t* acc_debug, const QuantOutArgs& qo, const ClusterArgs& qc,
+                        hipStream_t stream) {
     const bool dbg = acc_debug != nullptr;
     const void* k = a_bits == 3 ? pick<3>(w_bits, dbg) : a_bits == 4 ? pick<4>(w_bits, dbg) : pick<8>(w_bits, dbg);
     const int64_t tm = (M + Cfg::BM - 1) / Cfg::BM, tn = (N + Cfg::BN - 1) / Cfg::BN;
@@ -434,7 +499,7 @@ hipError_t launch_qgemm(const uint8_t* codes, int64_t M, int32_t N, int64_t a_ro
     int32_t arb = (int32_t)a_row_bytes, wrb = (int32_t)w_row_bytes;
     void* args[] = {(void*)&codes, (void*)&M, (void*)&arb, (void*)&w_packed, (void*)&N, (void*)&wrb,
                     (void*)&ga, (void*)&s_w, (void*)&colsum, (void*)&Y, (void*)&acc_debug,
-                    (void*)&tiles_m, (void*)&tiles_n};
+                    (void*)&tiles_m, (void*)&tiles_n, (void*)&qo, (void*)&qc};
     return hipLaunchKernel(k, dim3((unsigned)(tm * tn)), dim3(Cfg::NT), args, 0, stream);
 }
 

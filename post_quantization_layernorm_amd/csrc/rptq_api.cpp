@@ -195,9 +195,12 @@ int rptq_ln_reorder_quant(const void* x, int32_t in_mode, int64_t M, int32_t K,
                       "rptq_ln_reorder_quant launch");
 }
 
-int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N, const int32_t* bounds, int32_t g,
-               const float* s, const int32_t* z, int32_t a_bits, const uint8_t* w_packed, int32_t w_bits,
-               const float* s_w, const int32_t* colsum, float* Y, int32_t* acc_debug, void* stream) {
+// Shared by rptq_qgemm and rptq_qgemm_quant: validation of the GEMM proper,
+// the per-cluster tables, the launch.
+static int qgemm_common(const uint8_t* codes, int64_t M, int32_t K, int32_t N, const int32_t* bounds,
+                        int32_t g, const float* s, const int32_t* z, int32_t a_bits, const uint8_t* w_packed,
+                        int32_t w_bits, const float* s_w, const int32_t* colsum, float* Y, int32_t* acc_debug,
+                        const QuantOutArgs& qo, const ClusterArgs& qc, void* stream, const char* what) {
     if (M < 0) return fail(RPTQ_ERR_INVALID_ARG, "M = %lld < 0", (long long)M);
     if (K < 1 || N < 1) return fail(RPTQ_ERR_INVALID_ARG, "K = %d, N = %d must be >= 1", K, N);
     if (!valid_bits(a_bits)) return fail(RPTQ_ERR_INVALID_ARG, "a_bits = %d not in {3, 4, 8}", a_bits);
@@ -207,10 +210,10 @@ int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N, const int3
     if ((st = check_params(s, z, g))) return st;
     if (K > kMaxK) return fail(RPTQ_ERR_UNSUPPORTED, "K = %d exceeds %d", K, kMaxK);
     if (M == 0) return ok();
-    if (!codes || !w_packed || !s_w || !colsum || !Y)
-        return fail(RPTQ_ERR_INVALID_ARG, "codes, w_packed, s_w, colsum and Y must be non-NULL");
-    if (!aligned16(codes) || !aligned16(w_packed) || !aligned16(s_w) || !aligned16(colsum) || !aligned16(Y) ||
-        (acc_debug && !aligned16(acc_debug)))
+    if (!codes || !w_packed || !s_w || !colsum || (!Y && !qo.q_codes))
+        return fail(RPTQ_ERR_INVALID_ARG, "codes, w_packed, s_w, colsum and the output must be non-NULL");
+    if (!aligned16(codes) || !aligned16(w_packed) || !aligned16(s_w) || !aligned16(colsum) ||
+        (Y && !aligned16(Y)) || (acc_debug && !aligned16(acc_debug)) || (qo.q_codes && !aligned16(qo.q_codes)))
         return fail(RPTQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
     GemmArgs ga;
     std::memset(&ga, 0, sizeof ga);
@@ -233,8 +236,39 @@ int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N, const int3
     const int64_t a_row_bytes = (int64_t)steps * 32 * a_bits / 8;
     const int64_t w_row_bytes = (int64_t)steps * 32 * w_bits / 8;
     return hip_status(launch_qgemm(codes, M, N, a_row_bytes, a_bits, w_packed, w_row_bytes, w_bits, ga, s_w,
-                                   colsum, Y, acc_debug, (hipStream_t)stream),
-                      "rptq_qgemm launch");
+                                   colsum, Y, acc_debug, qo, qc, (hipStream_t)stream),
+                      what);
+}
+
+int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N, const int32_t* bounds, int32_t g,
+               const float* s, const int32_t* z, int32_t a_bits, const uint8_t* w_packed, int32_t w_bits,
+               const float* s_w, const int32_t* colsum, float* Y, int32_t* acc_debug, void* stream) {
+    if (M > 0 && !Y) return fail(RPTQ_ERR_INVALID_ARG, "Y must be non-NULL");
+    QuantOutArgs qo{nullptr, 0, 0};
+    ClusterArgs qc;
+    std::memset(&qc, 0, sizeof qc);
+    return qgemm_common(codes, M, K, N, bounds, g, s, z, a_bits, w_packed, w_bits, s_w, colsum, Y, acc_debug,
+                        qo, qc, stream, "rptq_qgemm launch");
+}
+
+int rptq_qgemm_quant(const uint8_t* codes, int64_t M, int32_t K, int32_t N_pad, const int32_t* bounds,
+                     int32_t g, const float* s, const int32_t* z, int32_t a_bits, const uint8_t* w_packed,
+                     int32_t w_bits, const float* s_w, const int32_t* colsum, int32_t act,
+                     const int32_t* out_bounds, int32_t out_g, const float* out_s, const int32_t* out_z,
+                     int32_t out_bits, uint8_t* out_codes, float* Y, void* stream) {
+    if (act != RPTQ_ACT_NONE && act != RPTQ_ACT_RELU) return fail(RPTQ_ERR_INVALID_ARG, "act = %d", act);
+    if (!valid_bits(out_bits)) return fail(RPTQ_ERR_INVALID_ARG, "out_bits = %d not in {3, 4, 8}", out_bits);
+    int st = check_bounds(out_bounds, out_g, -1);
+    if (st) return st;
+    if ((st = check_params(out_s, out_z, out_g))) return st;
+    if (N_pad != kpad_of(out_bounds, out_g))
+        return fail(RPTQ_ERR_INVALID_ARG, "N_pad = %d is not the output layout's K_pad %d", N_pad,
+                    kpad_of(out_bounds, out_g));
+    if (M > 0 && !out_codes) return fail(RPTQ_ERR_INVALID_ARG, "out_codes must be non-NULL");
+    QuantOutArgs qo{out_codes, (int64_t)N_pad * out_bits / 8, act};
+    const ClusterArgs qc = make_cluster_args(out_bounds, out_g, out_s, out_z, out_bits, true);
+    return qgemm_common(codes, M, K, N_pad, bounds, g, s, z, a_bits, w_packed, w_bits, s_w, colsum, Y, nullptr,
+                        qo, qc, stream, "rptq_qgemm_quant launch");
 }
 
 static int kv_checks(int64_t T, int32_t C, const int32_t* bounds, int32_t g, const float* s, const int32_t* z,
@@ -523,6 +557,35 @@ int rptq_pack_weights(const int8_t* wq, int32_t K, int32_t N, int32_t w_bits, co
         });
     for (auto& th : pool) th.join();
     return ok();
+}
+
+int rptq_pack_weights_out(const int8_t* wq, int32_t K, int32_t N, int32_t w_bits, const int32_t* R,
+                          const int32_t* bounds, int32_t g, const int32_t* R_out, const int32_t* out_bounds,
+                          int32_t out_g, const float* s_w, uint8_t* w_packed, int32_t* colsum, float* s_w_out) {
+    if (!wq || !s_w || !w_packed || !colsum || !s_w_out) return fail(RPTQ_ERR_INVALID_ARG, "NULL argument");
+    if (K < 1 || N < 1) return fail(RPTQ_ERR_INVALID_ARG, "K = %d, N = %d", K, N);
+    int st = check_bounds(out_bounds, out_g, N);
+    if (st) return st;
+    const int32_t np = kpad_of(out_bounds, out_g);
+    // padded output position -> natural output feature (-1 for pad)
+    std::vector<int32_t> src(np, -1);
+    std::vector<char> seen(N, 0);
+    int32_t off = 0;
+    for (int c = 0; c < out_g; ++c) {
+        for (int32_t j = out_bounds[c]; j < out_bounds[c + 1]; ++j) {
+            const int32_t n = R_out ? R_out[j] : j;
+            if (n < 0 || n >= N || seen[n]) return fail(RPTQ_ERR_INVALID_ARG, "R_out is not a permutation");
+            seen[n] = 1;
+            src[off + j - out_bounds[c]] = n;
+        }
+        off += (out_bounds[c + 1] - out_bounds[c] + 31) / 32 * 32;
+    }
+    std::vector<int8_t> wq2((size_t)K * np, 0);
+    for (int64_t k = 0; k < K; ++k)
+        for (int32_t p = 0; p < np; ++p)
+            if (src[p] >= 0) wq2[k * np + p] = wq[k * N + src[p]];
+    for (int32_t p = 0; p < np; ++p) s_w_out[p] = src[p] >= 0 ? s_w[src[p]] : 1.0f;
+    return rptq_pack_weights(wq2.data(), K, np, w_bits, R, bounds, g, w_packed, colsum);
 }
 
 }  // extern "C"

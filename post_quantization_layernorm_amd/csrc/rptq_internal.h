@@ -74,10 +74,20 @@ hipError_t launch_calib_minmax(const uint16_t* x, int mode, int64_t M, int32_t K
                                const float* gamma, const float* beta, float eps,
                                float* mx, float* mn, hipStream_t stream);
 
+// Quantized output of the GEMM (the epilogue quantizes Y for the next layer):
+// q_codes null = none.  N is then the next layer's SEG32 K_pad and column n
+// the padded position n; act 1 applies ReLU to Y first.
+struct QuantOutArgs {
+    uint8_t* q_codes;                      // device [M][q_row_bytes] SEG32, or null
+    int64_t q_row_bytes;
+    int32_t act;
+};
+
 hipError_t launch_qgemm(const uint8_t* codes, int64_t M, int32_t N, int64_t a_row_bytes,
                         int a_bits, const uint8_t* w_packed, int64_t w_row_bytes, int w_bits,
                         const GemmArgs& ga, const float* s_w, const int32_t* colsum,
-                        float* Y, int32_t* acc_debug, hipStream_t stream);
+                        float* Y, int32_t* acc_debug, const QuantOutArgs& qo, const ClusterArgs& qc,
+                        hipStream_t stream);
 
 // Number of workgroups a persistent streaming kernel should launch: the
 // device's compute units times the resident workgroups per unit.

@@ -115,6 +115,54 @@ def test_qgemm_m0_is_noop(P):
     assert _gemm(P, M=0, codes=None, Y=None) == 0
 
 
+def _gemm_q(P, **kw):
+    # output layout: clusters of 20 and 40 channels -> K_pad 32 + 64 = 96
+    a = dict(codes=FAKE, M=8, K=64, N=96, bounds=np.array([0, 16, 64], np.int32),
+             s=np.array([0.1, 0.2], np.float32), z=np.array([3, -2], np.int32), a_bits=4, w=FAKE, w_bits=4,
+             s_w=FAKE, colsum=FAKE, act=1, ob=np.array([0, 20, 60], np.int32),
+             os=np.array([0.5, 0.25], np.float32), oz=np.array([1, 2], np.int32), obits=4, out=FAKE, Y=None)
+    a.update(kw)
+    return P.lib().rptq_qgemm_quant(a["codes"], a["M"], a["K"], a["N"], _vp(a["bounds"]), a["bounds"].size - 1,
+                                    _vp(a["s"]), _vp(a["z"]), a["a_bits"], a["w"], a["w_bits"], a["s_w"],
+                                    a["colsum"], a["act"], _vp(a["ob"]), a["ob"].size - 1, _vp(a["os"]),
+                                    _vp(a["oz"]), a["obits"], a["out"], a["Y"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=64), -1), (dict(act=2), -1), (dict(obits=5), -1), (dict(out=None), -1),
+    (dict(os=np.array([0.5, 0.0], np.float32)), -1), (dict(ob=np.array([0, 20, 20], np.int32)), -1),
+    (dict(w_bits=2), -1), (dict(out=MISALIGNED), -3), (dict(Y=MISALIGNED), -3),
+])
+def test_qgemm_quant_rejects(P, kw, status):
+    assert _gemm_q(P, **kw) == status
+
+
+def test_qgemm_quant_m0_is_noop(P):
+    assert _gemm_q(P, M=0, codes=None, out=None) == 0
+
+
+def test_host_pack_weights_out_orders_and_pads_outputs(P, orc):
+    r = np.random.default_rng(5)
+    K, N = 64, 50
+    wq = r.integers(-7, 8, (K, N)).astype(np.int8)
+    s_w = r.uniform(0.5, 2.0, N).astype(np.float32)
+    R_out = r.permutation(N).astype(np.int32)
+    ob = np.array([0, 3, 40, 50], np.int32)             # padded: 32 + 64 + 32 = 128
+    wp, cs, swo = P.rptq_pack_weights_out(wq, None, np.array([0, K], np.int32), 4, R_out, ob, s_w)
+    wp_ref, cs_ref = P.rptq_pack_weights(wq, None, np.array([0, K], np.int32), 4)
+    assert wp.shape[0] == cs.shape[1] == swo.size == orc.seg32_kpad(ob) == 128
+    off = 0
+    for c in range(3):
+        n_c = ob[c + 1] - ob[c]
+        src = R_out[ob[c]:ob[c + 1]]
+        assert np.array_equal(wp[off:off + n_c], wp_ref[src])
+        assert np.array_equal(cs[:, off:off + n_c], cs_ref[:, src])
+        assert np.array_equal(swo[off:off + n_c], s_w[src])
+        pad = slice(off + n_c, off + (n_c + 31) // 32 * 32)
+        assert not wp[pad].any() and not cs[:, pad].any() and (swo[pad] == 1.0).all()
+        off += (n_c + 31) // 32 * 32
+
+
 def _kv(P, fn, **kw):
     a = dict(src=FAKE, T=10, C=64, R=None, bounds=np.array([0, 32, 64], np.int32),
              s=np.array([0.1, 0.2], np.float32), z=np.array([3, -2], np.int32), bits=3, dst=FAKE)

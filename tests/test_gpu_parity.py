@@ -229,6 +229,48 @@ def test_end_to_end_ln_then_gemm(P, ab, wb):
     assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
 
 
+# ----------------------------------------------------------------------------- GEMM with quantized output
+@pytest.mark.parametrize("ab,wb,ob,act,N", [(4, 4, 4, 1, 330), (3, 3, 3, 1, 200), (8, 4, 8, 0, 130),
+                                             (4, 4, 3, 1, 1024)])
+def test_qgemm_quant_output(P, ab, wb, ob, act, N):
+    """The epilogue quantizes the (activated) output for the next layer: the
+    codes equal the oracle's quantization of the kernel's own y bit for bit,
+    y matches the oracle's GEMM, and against the oracle end to end at most
+    0.1% of the codes differ, by 1."""
+    M, K, g, g2 = 150, 2048, 8, 6
+    _say("gemm quant-out", ab, wb, ob, act, N)
+    c = layer_case(M, K, N, g, ab, wb, seed=500 + N + ab)
+    q, codes = _oracle_codes(c)
+    Y_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w)
+    a_o = np.maximum(Y_o, np.float32(0)) if act else Y_o
+    omx, omn = orc.channel_minmax(a_o)
+    R2, b2, s2, z2 = orc.calibrate(omx, omn, g2, ob, synthetic.kmeans_uniforms(N, 2, g2), n_init=2)
+    want, y_want = orc.qgemm_quant(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w, act, R2, b2, s2, z2, ob,
+                                   return_y=True)
+    wp, cs, swo = P.rptq_pack_weights_out(c.Wq, c.R, c.bounds, wb, R2, b2, c.s_w)
+    npad = orc.seg32_kpad(b2)
+    yd = torch.full((M, npad), 7.0, dtype=torch.float32, device="cuda")
+    got = P.rptq_qgemm_quant(dev(codes), M, K, npad, c.bounds, c.s, c.z, ab, dev(wp), wb, dev(swo), dev(cs), act,
+                             b2, s2, z2, ob, y_out=yd)
+    got = got.cpu().numpy(); yg = yd.cpu().numpy()
+    # padded position of each real output channel (in R2 order)
+    pos = np.concatenate([orc.seg32_kpad(b2[:c2 + 1]) + np.arange(b2[c2 + 1] - b2[c2]) for c2 in range(g2)])
+    real = np.zeros(npad, bool); real[pos] = True
+    assert not yg[:, ~real].any()
+    y_real = np.ascontiguousarray(yg[:, pos])
+    assert rel_l2(y_real, y_want) <= 1e-3
+    if act:
+        assert (y_real >= 0).all()
+    # bit-exact on the kernel's own y
+    assert np.array_equal(got, orc.pack_seg32(orc.quantize(y_real, b2, s2, z2, ob), b2, ob))
+    # end to end
+    qg, pad = orc.unpack_seg32(got, N, b2, ob, return_pad=True)
+    qw = orc.unpack_seg32(want, N, b2, ob)
+    d = np.abs(qg.astype(np.int32) - qw.astype(np.int32))
+    assert not pad.any()
+    assert d.max() <= 1 and (d > 0).mean() <= 1e-3, (d.max(), (d > 0).mean())
+
+
 # ----------------------------------------------------------------------------- calibration
 def test_calib_minmax_matches_oracle(P):
     K = 1024

@@ -419,6 +419,43 @@ def test_qgemm_matches_dequantized_matmul_realistic(orc):
     np.testing.assert_allclose(Y.astype(np.float64), ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("out_bits", [3, 4, 8])
+def test_qgemm_quant_error_bound_and_order_invariance(orc, out_bits):
+    """The epilogue-quantized output of a reordered linear layer: every code
+    dequantizes to within s_c / 2 of the activated output (values inside the
+    calibrated cluster range), pads are 0, and the code of an output channel
+    does not depend on where inside its cluster the channel is placed."""
+    K, N, M, g, g2 = 128, 96, 24, 4, 5
+    mu, sg = synthetic.channel_params(K, 31, 0.02)
+    x = synthetic.tokens(M, mu, sg, 31, synthetic.STREAM_EVAL)
+    gamma, beta = synthetic.ln_params(K, 31)
+    y_in = orc.layernorm(x, gamma, beta)
+    mx, mn = orc.channel_minmax(y_in)
+    R, bounds, s, z = orc.calibrate(mx, mn, g, 4, synthetic.kmeans_uniforms(31, 2, g), n_init=2)
+    q = orc.quantize(orc.layernorm(x, gamma, beta, 1e-5, R), bounds, s, z, 4)
+    Wq, s_w = orc.quantize_weights(synthetic.weights(K, N, 31), 4)
+    act = np.maximum(orc.qgemm(q, Wq, R, bounds, s, z, s_w), np.float32(0))
+    omx, omn = orc.channel_minmax(act)
+    R2, b2, s2, z2 = orc.calibrate(omx, omn, g2, out_bits, synthetic.kmeans_uniforms(32, 2, g2), n_init=2)
+    codes, y = orc.qgemm_quant(q, Wq, R, bounds, s, z, s_w, 1, R2, b2, s2, z2, out_bits, return_y=True)
+    assert np.array_equal(y, act[:, R2])
+    qo, pad = orc.unpack_seg32(codes, N, b2, out_bits, return_pad=True)
+    assert not pad.any()
+    dq = orc.dequantize(qo, b2, s2, z2).astype(np.float64)
+    for c in range(g2):
+        sl = slice(b2[c], b2[c + 1])
+        assert np.all(np.abs(dq[:, sl] - y[:, sl]) <= s2[c] / 2 * (1 + 1e-6) + 1e-12), c
+    # the same partition, members in reverse order inside each cluster
+    R3 = R2.copy()
+    for c in range(g2):
+        R3[b2[c]:b2[c + 1]] = R2[b2[c]:b2[c + 1]][::-1]
+    q3 = orc.unpack_seg32(orc.qgemm_quant(q, Wq, R, bounds, s, z, s_w, 1, R3, b2, s2, z2, out_bits), N, b2,
+                          out_bits)
+    nat2 = np.empty_like(qo); nat2[:, R2] = qo
+    nat3 = np.empty_like(q3); nat3[:, R3] = q3
+    assert np.array_equal(nat2, nat3)
+
+
 @pytest.mark.parametrize("wbits", [3, 4, 8])
 def test_weight_quantization_bounds(orc, wbits):
     W = synthetic.weights(64, 40, 3)
