@@ -55,7 +55,10 @@ def source_hash(files):
 
 
 KERNEL_SOURCES = {
-    "qgemm": ["post_quantization_layernorm_amd/csrc/qgemm.hip"],
+    "qgemm": ["post_quantization_layernorm_amd/csrc/qgemm.hip",
+              "post_quantization_layernorm_amd/csrc/rptq_device.hpp"],
+    "qgemm_quant_out": ["post_quantization_layernorm_amd/csrc/qgemm.hip",
+                        "post_quantization_layernorm_amd/csrc/rptq_device.hpp"],
     "ln_reorder_quant": ["post_quantization_layernorm_amd/csrc/ln_quant.hip",
                          "post_quantization_layernorm_amd/csrc/rptq_device.hpp"],
     "kv_quant_pack": ["post_quantization_layernorm_amd/csrc/kv.hip",
@@ -126,7 +129,6 @@ def main():
         wp, cs = P.rptq_pack_weights(wq, R, bounds, wb)
         wts[wb] = (torch.from_numpy(wp).to(dev), torch.from_numpy(cs).to(dev), torch.from_numpy(s_w).to(dev))
         del wq, wp
-    del W
     variants = {}
     for ab in (4, 3):
         s, z = P.rptq_cluster_params(mx, mn, R, bounds, ab)
@@ -135,6 +137,26 @@ def main():
     Y = torch.empty((M, N), dtype=torch.float32, device=dev)
     kpad = P.rptq_codes_kpad(bounds)
     log(f"[bench] weights ready, K_pad={kpad} ({time.time() - t_setup:.1f}s)")
+
+    # fc1 with its output quantized for fc2 (ReLU, then fc2's 4-bit clusters):
+    # fc2's input clusters come from fc1's own output on the calibration tokens
+    v4 = variants[4]
+    cc = P.rptq_ln_reorder_quant(xc, R_d, gr_d, br_d, bounds, v4["s"], v4["z"], 4)
+    wp_d, cs_d, sw_d = wts[w.w_bits]
+    yc = torch.relu(P.rptq_qgemm(cc, xc.shape[0], K, N, bounds, v4["s"], v4["z"], 4, wp_d, w.w_bits, sw_d, cs_d))
+    omx, omn = yc.amax(0).cpu().numpy(), yc.amin(0).cpu().numpy()
+    del cc, yc
+    R2, b2 = P.rptq_kmeans_reorder(omx, omn, g, synthetic.kmeans_uniforms(w.seed + 1, 10, g), n_init=10)
+    s2, z2 = P.rptq_cluster_params(omx, omn, R2, b2, 4)
+    wq, s_w = P.rptq_quantize_weights(W, w.w_bits)
+    wpo, cso, swo = P.rptq_pack_weights_out(wq, R, bounds, w.w_bits, R2, b2, s_w)
+    del wq, W
+    n_pad = P.rptq_codes_kpad(b2)
+    qout = dict(w=torch.from_numpy(wpo).to(dev), cs=torch.from_numpy(cso).to(dev), sw=torch.from_numpy(swo).to(dev),
+                bounds=b2, s=s2, z=z2, n_pad=n_pad,
+                codes=torch.empty((M, P.rptq_codes_row_bytes(b2, 4)), dtype=torch.uint8, device=dev))
+    del wpo
+    log(f"[bench] fc2 input clusters ready, N_pad={n_pad} ({time.time() - t_setup:.1f}s)")
 
     # ------------------------------------------------------------------ OPT-66B KV cache
     kvw = synthetic.KV_WORKLOADS["opt66b_kv_a3"]
@@ -159,7 +181,7 @@ def main():
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ one step
-    names = ["ln4", "gemm4", "ln3", "gemm3", "gemm3w3", "kvq_K", "kvq_V", "kvd_K", "kvd_V"]
+    names = ["ln4", "gemm4", "ln3", "gemm3", "gemm3w3", "gemm4q", "kvq_K", "kvq_V", "kvd_K", "kvd_V"]
 
     def step(ev=None):
         def rec(i):
@@ -181,6 +203,13 @@ def main():
                 P.rptq_qgemm(v["codes"], M, K, N, bounds, v["s"], v["z"], ab, wp_d, 3, sw_d, cs_d, out=Y,
                              stream=stream)
                 k += 1
+        rec(k)
+        # fc1 on the 4-bit codes, output quantized for fc2
+        v = variants[4]
+        P.rptq_qgemm_quant(v["codes"], M, K, qout["n_pad"], bounds, v["s"], v["z"], 4, qout["w"], w.w_bits,
+                           qout["sw"], qout["cs"], P.RPTQ_ACT_RELU, qout["bounds"], qout["s"], qout["z"], 4,
+                           out=qout["codes"], stream=stream)
+        k += 1
         rec(k)
         for name in ("K", "V"):
             d = kv[name]
@@ -272,6 +301,9 @@ def main():
         "ln_quant_frac_hbm_peak": res_layer[4]["ln_frac_hbm_peak"],
         "w4a3": res_layer[3],
         "w4a4": res_layer[4],
+        "w4a4_quant_out": {"gemm_ms": avg["gemm4q"] * 1e3, "gemm_tops": ops / avg["gemm4q"] / 1e12,
+                           "gemm_frac_int8_peak": ops / avg["gemm4q"] / 1e12 / INT8_PEAK_TOPS,
+                           "n_pad": n_pad, "out": "ReLU, fc2's 4-bit per-cluster codes (SEG32)"},
         "w3a3": {"gemm_ms": avg["gemm3w3"] * 1e3, "gemm_tops": ops / avg["gemm3w3"] / 1e12,
                  "gemm_frac_int8_peak": ops / avg["gemm3w3"] / 1e12 / INT8_PEAK_TOPS,
                  "tokens_per_s": M / (avg["ln3"] + avg["gemm3w3"])},
@@ -294,11 +326,16 @@ def main():
 
 
 # Kernels whose HBM traffic bench.py reports, matched on rocprofv3's kernel
-# names: the W4A4 GEMM, the 4-bit fused LayerNorm-quant, the 3-bit KV pack.
+# names (pattern, which matching dispatch of the one-step counter run: an
+# index in dispatch order, or None for the mean of all): the W4A4 GEMM (the
+# step's first 4-4 GEMM; the last is fc1 with its output quantized for fc2),
+# the 4-bit fused LayerNorm-quant (the step's, after the calibration one), the
+# 3-bit KV pack (K and V).
 PMC_KERNELS = {
-    "qgemm": "qgemm_kernel<4, 4, false",
-    "ln_reorder_quant": "ln_reorder_quant_kernel<4, 0,",
-    "kv_quant_pack": "kv_quant_pack_kernel<3,",
+    "qgemm": ("qgemm_kernel<4, 4, false", -2),
+    "qgemm_quant_out": ("qgemm_kernel<4, 4, false", -1),
+    "ln_reorder_quant": ("ln_reorder_quant_kernel<4, 0,", -1),
+    "kv_quant_pack": ("kv_quant_pack_kernel<3,", None),
 }
 COPY_PROBE_BYTES = 1 << 30
 
@@ -333,13 +370,14 @@ def ingest_pmc(fetch_csv, write_csv):
         probe = d[max(copies)][1] * 1024.0
         scale[counter] = COPY_PROBE_BYTES / probe
         per[counter] = d
-    for key, pat in PMC_KERNELS.items():
+    for key, (pat, pick) in PMC_KERNELS.items():
         vals = {}
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-            v = [x for n, x in per[counter].values() if pat in n]
+            v = [x for _, (n, x) in sorted(per[counter].items()) if pat in n]
             if not v:
                 break
-            vals[counter] = float(np.mean(v)) * 1024.0 * scale[counter]
+            x = float(np.mean(v)) if pick is None else v[pick]
+            vals[counter] = x * 1024.0 * scale[counter]
         if len(vals) == 2:
             res[key] = {"source_hash": source_hash(KERNEL_SOURCES[key]),
                         "bytes_per_launch": vals["FETCH_SIZE"] + vals["WRITE_SIZE"],
