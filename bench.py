@@ -177,11 +177,17 @@ def main():
         kv[name] = dict(x=data, R=torch.from_numpy(kR).to(dev), bounds=kbnd, s=ks, z=kz,
                         packed=torch.empty((T, P.rptq_kv_row_bytes(C, kvb)), dtype=torch.uint8, device=dev),
                         out=torch.empty((T, C), dtype=torch.float16, device=dev))
+    # decode attention over the packed caches: 64 sequences x 8192 tokens, 72 heads x 128
+    AB, AD = 64, 128
+    AT = T // AB
+    q_att = torch.from_numpy((np.random.default_rng(5).standard_normal((AB, C)) * 0.25).astype(np.float16)).to(dev)
+    att_ws = torch.empty(P.rptq_kv_attention_workspace_bytes(AB, AT, C, AD), dtype=torch.uint8, device=dev)
+    att_out = torch.empty((AB, C), dtype=torch.float32, device=dev)
     log(f"[bench] KV caches ready ({time.time() - t_setup:.1f}s)")
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ one step
-    names = ["ln4", "gemm4", "ln3", "gemm3", "gemm3w3", "gemm4q", "kvq_K", "kvq_V", "kvd_K", "kvd_V"]
+    names = ["ln4", "gemm4", "ln3", "gemm3", "gemm3w3", "gemm4q", "kvq_K", "kvq_V", "kvd_K", "kvd_V", "kv_attn"]
 
     def step(ev=None):
         def rec(i):
@@ -222,6 +228,12 @@ def main():
                               stream=stream)
             k += 1
             rec(k)
+        dk, dv = kv["K"], kv["V"]
+        P.rptq_kv_attention(q_att, dk["packed"], dv["packed"], AB, AT, C, AD, float(1.0 / np.sqrt(AD)),
+                            (dk["R"], dk["bounds"], dk["s"], dk["z"]), (dv["R"], dv["bounds"], dv["s"], dv["z"]),
+                            kvb, out=att_out, workspace=att_ws, stream=stream)
+        k += 1
+        rec(k)
 
     for _ in range(args.warmup):
         step()
@@ -260,6 +272,12 @@ def main():
     out["kv_dequant_GBps"] = kv_bytes / td / 1e9
     out["kv_pack_ms"] = tq * 1e3
     out["kv_dequant_ms"] = td * 1e3
+    att_bytes = 2 * T * C * kvb / 8
+    out["kv_attention"] = {"ms": avg["kv_attn"] * 1e3, "GBps": att_bytes / avg["kv_attn"] / 1e9,
+                           "frac_hbm_peak": att_bytes / avg["kv_attn"] / 1e9 / HBM_PEAK_GBPS,
+                           "shape": f"{AB} sequences x {AT} tokens, {C // AD} heads x {AD}, {kvb}-bit K and V",
+                           "bytes": "packed K + V read once (the dequantize path writes and rereads "
+                                    f"{2 * T * C * 2 / 1e9:.1f} GB of fp16)"}
 
     gemm_ops_launch = ops
     t_gemm = avg["gemm4"]

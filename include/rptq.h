@@ -210,6 +210,38 @@ int rptq_kv_dequant(const uint8_t* packed, int64_t T, int32_t C, const int32_t* 
                     const int32_t* bounds, int32_t g, const float* s, const int32_t* z,
                     int32_t bits, uint16_t* out, void* stream);
 
+/*
+ * Decode attention that reads the packed caches directly (RPTQ write-up,
+ * evaluation: the KV-cache settings keep keys and values quantized; this is
+ * where they are read back).  One query token per sequence b:
+ *   K, V        = the caches rptq_kv_dequant would produce from k_packed,
+ *                 v_packed (fp16 values fp16_rne(s_c (q - z_c)), natural
+ *                 channel order), rows b*T .. b*T + T - 1 of sequence b
+ *   score[h][t] = scale * sum_d q[b][h*head_dim + d] * K[b*T + t][h*head_dim + d]
+ *   out[b][h*head_dim + d] = sum_t softmax_t(score[h])[t] * V[b*T + t][h*head_dim + d]
+ * without materializing K or V: every packed row is dequantized into on-chip
+ * memory and consumed there.
+ * q        device fp16 [B][C], natural order;  out device fp32 [B][C].
+ * k_packed, v_packed  device [B*T][rptq_kv_row_bytes(C, bits)] (outputs of
+ *          rptq_kv_quant_pack), each with its own R (device [C] or NULL),
+ *          bounds, s, z (host), as given to rptq_kv_quant_pack.
+ * head_dim 64 or 128 (RPTQ_ERR_UNSUPPORTED otherwise); C a multiple of 128,
+ *          at most 10240 (OPT-66B: 9216); T >= 1; bits in {3, 4, 8}; scale > 0 (usually
+ *          1/sqrt(head_dim)).
+ * workspace device, >= rptq_kv_attention_workspace_bytes(B, T, C, head_dim)
+ *          bytes, 16-byte aligned, owned by the caller (per-chunk partial
+ *          outputs and softmax statistics; contents need not be initialized).
+ * B = 0 is a no-op.  Errors as rptq_kv_quant_pack.
+ */
+int rptq_kv_attention(const uint16_t* q, const uint8_t* k_packed, const uint8_t* v_packed,
+                      int32_t B, int32_t T, int32_t C, int32_t head_dim, float scale,
+                      const int32_t* R_k, const int32_t* bounds_k, int32_t g_k, const float* s_k, const int32_t* z_k,
+                      const int32_t* R_v, const int32_t* bounds_v, int32_t g_v, const float* s_v, const int32_t* z_v,
+                      int32_t bits, float* out, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes rptq_kv_attention needs; -1 on invalid sizes. */
+int64_t rptq_kv_attention_workspace_bytes(int32_t B, int32_t T, int32_t C, int32_t head_dim);
+
 /* ---------------------------------------------------------- calibration
  * Offline steps that produce R, bounds, s, z (RPTQ write-up, method section:
  * run calibration data, record each channel's max and min, KMeans on the

@@ -319,6 +319,30 @@ def kv_quant_pack(kv_f16, R, bounds, s, z, bits) -> np.ndarray:
     return out
 
 
+def kv_attention(q_f16, k_packed, v_packed, B, T, C, head_dim, scale, k_params, v_params, bits):
+    """Decode attention over a packed K/V cache (RPTQ write-up, evaluation:
+    the KV-cache settings keep the keys and values quantized because they
+    hold most of the memory; attention reads them back).  The cache is what
+    kv_dequant produces from the packed rows (fp16, natural order); per
+    sequence b, head h (channels h*head_dim .. +head_dim) and token t:
+      score[h][t] = scale * sum_d q[b][h, d] * K[b*T + t][h, d]
+      p[h][t]     = exp(score[h][t] - max_t score[h]) / sum_t exp(...)
+      out[b][h, d] = sum_t p[h][t] * V[b*T + t][h, d]
+    in fp64.  q_f16: fp16 bit patterns [B][C]; k_params / v_params:
+    (R, bounds, s, z).  Returns fp64 [B][C]."""
+    H = C // head_dim
+    Kc = half_to_double(kv_dequant(k_packed, C, *k_params, bits)).reshape(B, T, H, head_dim)
+    Vc = half_to_double(kv_dequant(v_packed, C, *v_params, bits)).reshape(B, T, H, head_dim)
+    q = half_to_double(np.asarray(q_f16).view(np.uint16)).reshape(B, H, head_dim)
+    out = np.empty((B, H, head_dim), np.float64)
+    for b in range(B):
+        sc = np.einsum("hd,thd->ht", q[b], Kc[b]) * float(scale)
+        sc = np.exp(sc - sc.max(axis=1, keepdims=True))
+        p = sc / sc.sum(axis=1, keepdims=True)
+        out[b] = np.einsum("ht,thd->hd", p, Vc[b])
+    return out.reshape(B, C)
+
+
 def kv_dequant(packed, C, R, bounds, s, z, bits) -> np.ndarray:
     """Returns fp16 bit patterns (uint16) [T][C] in natural order."""
     p = _c(packed, np.uint8); T = p.shape[0]

@@ -36,6 +36,7 @@ RPTQ_MAX_K = 16384
 
 EXPORTED = [
     "rptq_ln_reorder_quant", "rptq_qgemm", "rptq_qgemm_quant", "rptq_kv_quant_pack", "rptq_kv_dequant",
+    "rptq_kv_attention", "rptq_kv_attention_workspace_bytes",
     "rptq_calib_minmax", "rptq_kmeans_reorder", "rptq_cluster_params", "rptq_quantize_weights",
     "rptq_pack_weights", "rptq_pack_weights_out", "rptq_codes_kpad", "rptq_codes_row_bytes", "rptq_weights_row_bytes",
     "rptq_kv_row_bytes", "rptq_status_string", "rptq_last_error", "rptq_version",
@@ -75,6 +76,9 @@ def lib() -> ctypes.CDLL:
                                         _P, _I32, _P, _P, _I32, _P, _P, _P]),
             "rptq_kv_quant_pack": (_I32, [_P, _I64, _I32, _P, _P, _I32, _P, _P, _I32, _P, _P]),
             "rptq_kv_dequant": (_I32, [_P, _I64, _I32, _P, _P, _I32, _P, _P, _I32, _P, _P]),
+            "rptq_kv_attention": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _I32, _P, _P,
+                                         _P, _P, _I32, _P, _P, _I32, _P, _P, _I64, _P]),
+            "rptq_kv_attention_workspace_bytes": (_I64, [_I32, _I32, _I32, _I32]),
             "rptq_calib_minmax": (_I32, [_P, _I32, _I64, _I32, _P, _P, ctypes.c_float, _P, _P, _P]),
             "rptq_kmeans_reorder": (_I32, [_P, _P, _I32, _I32, _P, _I32, _I32, _P, _P]),
             "rptq_cluster_params": (_I32, [_P, _P, _P, _P, _I32, _I32, _P, _P]),
@@ -217,6 +221,32 @@ def rptq_kv_quant_pack(kv, R, bounds, s, z, bits, out=None, stream=None):
     st = lib().rptq_kv_quant_pack(_dp(kv), T, C, _dp(R), _hp(b), b.size - 1, _hp(sh), _hp(zh), bits,
                                   _dp(out), _stream(stream))
     _check(st, "rptq_kv_quant_pack")
+    return out
+
+
+def rptq_kv_attention_workspace_bytes(B, T, C, head_dim) -> int:
+    return int(lib().rptq_kv_attention_workspace_bytes(B, T, C, head_dim))
+
+
+def rptq_kv_attention(q, k_packed, v_packed, B, T, C, head_dim, scale, k_params, v_params, bits, out=None,
+                      workspace=None, stream=None):
+    """Decode attention over packed K/V.  q: cuda fp16 [B][C]; k_params /
+    v_params: (R cuda int32 [C] or None, bounds, s, z).  Returns cuda fp32
+    [B][C]."""
+    Rk, bk, sk, zk = k_params
+    Rv, bv, sv, zv = v_params
+    bk = _h(bk, np.int32); sk = _h(sk, np.float32); zk = _h(zk, np.int32)
+    bv = _h(bv, np.int32); sv = _h(sv, np.float32); zv = _h(zv, np.int32)
+    if out is None:
+        out = torch.empty((B, C), dtype=torch.float32, device=q.device)
+    need = rptq_kv_attention_workspace_bytes(B, T, C, head_dim)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().rptq_kv_attention(_dp(q), _dp(k_packed), _dp(v_packed), B, T, C, head_dim, scale, _dp(Rk),
+                                 _hp(bk), bk.size - 1, _hp(sk), _hp(zk), _dp(Rv), _hp(bv), bv.size - 1,
+                                 _hp(sv), _hp(zv), bits, _dp(out), _dp(workspace), wsz, _stream(stream))
+    _check(st, "rptq_kv_attention")
     return out
 
 

@@ -18,7 +18,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librptq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["rptq_api.cpp", "ln_quant.hip", "kv.hip", "qgemm.hip", "calib.hip"]
+SOURCES = ["rptq_api.cpp", "ln_quant.hip", "kv.hip", "kv_attn.hip", "qgemm.hip", "calib.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]

@@ -299,6 +299,43 @@ int rptq_kv_quant_pack(const uint16_t* kv, int64_t T, int32_t C, const int32_t* 
                       "rptq_kv_quant_pack launch");
 }
 
+int64_t rptq_kv_attention_workspace_bytes(int32_t B, int32_t T, int32_t C, int32_t head_dim) {
+    if (B < 0 || T < 1 || (head_dim != 64 && head_dim != 128) || C < 128 || C % 128 || C > kAttnMaxC) return -1;
+    return kv_attention_workspace(B, T, C, head_dim);
+}
+
+int rptq_kv_attention(const uint16_t* q, const uint8_t* k_packed, const uint8_t* v_packed, int32_t B, int32_t T,
+                      int32_t C, int32_t head_dim, float scale, const int32_t* R_k, const int32_t* bounds_k,
+                      int32_t g_k, const float* s_k, const int32_t* z_k, const int32_t* R_v,
+                      const int32_t* bounds_v, int32_t g_v, const float* s_v, const int32_t* z_v, int32_t bits,
+                      float* out, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (B < 0) return fail(RPTQ_ERR_INVALID_ARG, "B = %d < 0", B);
+    if (T < 1) return fail(RPTQ_ERR_INVALID_ARG, "T = %d < 1", T);
+    if (head_dim != 64 && head_dim != 128) return fail(RPTQ_ERR_UNSUPPORTED, "head_dim = %d not 64 or 128", head_dim);
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(RPTQ_ERR_INVALID_ARG, "scale must be finite and > 0");
+    int st = kv_checks(T, C, bounds_k, g_k, s_k, z_k, bits);
+    if (st) return st;
+    if ((st = kv_checks(T, C, bounds_v, g_v, s_v, z_v, bits))) return st;
+    if (C % 128) return fail(RPTQ_ERR_UNSUPPORTED, "C = %d is not a multiple of 128", C);
+    if (C > kAttnMaxC) return fail(RPTQ_ERR_UNSUPPORTED, "C = %d exceeds %d", C, kAttnMaxC);
+    if ((int64_t)B * T > ((int64_t)1 << 31) / 2) return fail(RPTQ_ERR_UNSUPPORTED, "B * T too large");
+    if (B == 0) return ok();
+    if (!q || !k_packed || !v_packed || !out || !workspace)
+        return fail(RPTQ_ERR_INVALID_ARG, "q, k_packed, v_packed, out and workspace must be non-NULL");
+    if (!aligned16(q) || !aligned16(k_packed) || !aligned16(v_packed) || !aligned16(out) || !aligned16(workspace) ||
+        (R_k && !aligned16(R_k)) || (R_v && !aligned16(R_v)))
+        return fail(RPTQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    const int64_t need = kv_attention_workspace(B, T, C, head_dim);
+    if (workspace_bytes < need)
+        return fail(RPTQ_ERR_INVALID_ARG, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                    (long long)need);
+    const ClusterArgs ck = make_cluster_args(bounds_k, g_k, s_k, z_k, bits, false);
+    const ClusterArgs cv = make_cluster_args(bounds_v, g_v, s_v, z_v, bits, false);
+    return hip_status(launch_kv_attention(q, k_packed, v_packed, B, T, C, head_dim, scale, R_k, ck, R_v, cv, out,
+                                          workspace, (hipStream_t)stream),
+                      "rptq_kv_attention launch");
+}
+
 int rptq_kv_dequant(const uint8_t* packed, int64_t T, int32_t C, const int32_t* R, const int32_t* bounds,
                     int32_t g, const float* s, const int32_t* z, int32_t bits, uint16_t* out, void* stream) {
     int st = kv_checks(T, C, bounds, g, s, z, bits);

@@ -70,6 +70,16 @@ hipError_t launch_kv_quant_pack(const uint16_t* kv, int64_t T, int32_t C, const 
 hipError_t launch_kv_dequant(const uint8_t* packed, int64_t T, int32_t C, const int32_t* R,
                              const ClusterArgs& ca, uint16_t* out, hipStream_t stream);
 
+// Decode attention over packed K/V (chunked, then merged); workspace holds
+// the per-chunk partial outputs and softmax statistics.
+constexpr int kAttnMaxC = 5 * 256 * 8;   // 256 lanes x 5 units of 8 channels
+void kv_attention_geometry(int32_t T, int32_t C, int32_t D, int32_t& TC, int32_t& nch);
+int64_t kv_attention_workspace(int32_t B, int32_t T, int32_t C, int32_t D);
+hipError_t launch_kv_attention(const uint16_t* q, const uint8_t* kp, const uint8_t* vp, int32_t B, int32_t T,
+                               int32_t C, int32_t D, float scale, const int32_t* Rk, const ClusterArgs& ck,
+                               const int32_t* Rv, const ClusterArgs& cv, float* out, void* workspace,
+                               hipStream_t stream);
+
 hipError_t launch_calib_minmax(const uint16_t* x, int mode, int64_t M, int32_t K,
                                const float* gamma, const float* beta, float eps,
                                float* mx, float* mn, hipStream_t stream);

@@ -163,6 +163,40 @@ def test_host_pack_weights_out_orders_and_pads_outputs(P, orc):
         off += (n_c + 31) // 32 * 32
 
 
+def _attn(P, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=2, T=10, C=256, D=128, scale=0.088, Rk=None,
+             bk=np.array([0, 128, 256], np.int32), sk=np.array([0.1, 0.2], np.float32), zk=np.array([3, -2], np.int32),
+             Rv=None, bv=np.array([0, 256], np.int32), sv=np.array([0.3], np.float32), zv=np.array([1], np.int32),
+             bits=3, out=FAKE, ws=FAKE, wsz=1 << 30)
+    a.update(kw)
+    return P.lib().rptq_kv_attention(a["q"], a["k"], a["v"], a["B"], a["T"], a["C"], a["D"], a["scale"], a["Rk"],
+                                     _vp(a["bk"]), a["bk"].size - 1, _vp(a["sk"]), _vp(a["zk"]), a["Rv"],
+                                     _vp(a["bv"]), a["bv"].size - 1, _vp(a["sv"]), _vp(a["zv"]), a["bits"],
+                                     a["out"], a["ws"], a["wsz"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), -1), (dict(B=-1), -1), (dict(D=96), -2), (dict(scale=0.0), -1), (dict(scale=float("nan")), -1),
+    (dict(bits=5), -1), (dict(C=192, bk=np.array([0, 192], np.int32), bv=np.array([0, 192], np.int32),
+                              sk=np.array([0.1], np.float32), zk=np.array([0], np.int32)), -2),
+    (dict(C=10368, bk=np.array([0, 10368], np.int32), bv=np.array([0, 10368], np.int32),
+          sk=np.array([0.1], np.float32), zk=np.array([0], np.int32)), -2),
+    (dict(sv=np.array([-1.0], np.float32)), -1), (dict(out=None), -1), (dict(ws=None), -1), (dict(wsz=16), -1),
+    (dict(q=MISALIGNED), -3), (dict(ws=MISALIGNED), -3),
+])
+def test_kv_attention_rejects(P, kw, status):
+    assert _attn(P, **kw) == status
+
+
+def test_kv_attention_b0_noop_and_workspace_size(P):
+    assert _attn(P, B=0, q=None, k=None, v=None, out=None, ws=None, wsz=0) == 0
+    # 64 sequences x 8192 tokens, 9216 channels, head 128: 64 chunks of 128 tokens
+    n = P.rptq_kv_attention_workspace_bytes(64, 8192, 9216, 128)
+    assert n == 64 * 64 * 9216 * 4 + 64 * 64 * 72 * 2 * 4
+    assert P.rptq_kv_attention_workspace_bytes(1, 0, 256, 128) == -1
+    assert P.rptq_kv_attention_workspace_bytes(1, 5, 256, 96) == -1
+
+
 def _kv(P, fn, **kw):
     a = dict(src=FAKE, T=10, C=64, R=None, bounds=np.array([0, 32, 64], np.int32),
              s=np.array([0.1, 0.2], np.float32), z=np.array([3, -2], np.int32), bits=3, dst=FAKE)

@@ -118,3 +118,36 @@ def test_kv_fullsize_sampled(P):
     assert np.array_equal(packed[ri].cpu().numpy(), want_p)
     want_d = orc.kv_dequant(want_p, C, R, bounds, s, z, bits)
     assert np.array_equal(out[ri].cpu().numpy().view(np.uint16), want_d)
+
+
+def test_kv_attention_fullsize_sampled(P):
+    """Decode attention over the whole OPT-66B cache (64 sequences x 8192
+    tokens, 9216 channels = 72 heads x 128, 3 bit), in the launch the
+    benchmark times; the oracle checks two sequences, packing their rows
+    itself from the same fp16 cache rows."""
+    kw = synthetic.KV_WORKLOADS["opt66b_kv_a3"]
+    T, C, g, bits = kw.T, kw.C, kw.g, kw.bits
+    B, Ts, D = 64, T // 64, 128
+    _say("kv attention", B, Ts, C)
+    params, packed, raw = [], [], []
+    for k, (sch, scal, sev) in enumerate(((synthetic.STREAM_CHANNELS, synthetic.STREAM_CALIB, synthetic.STREAM_EVAL),
+                                          (synthetic.STREAM_CHANNELS_V, synthetic.STREAM_CALIB_V,
+                                           synthetic.STREAM_EVAL_V))):
+        mu, sg = synthetic.channel_params(C, kw.seed, kw.outlier_frac, stream=sch)
+        mx, mn = orc.channel_minmax(synthetic.tokens(kw.calib_tokens, mu, sg, kw.seed, scal))
+        par = orc.calibrate(mx, mn, g, bits, synthetic.kmeans_uniforms(kw.seed + k, 3, g), n_init=3)
+        x = synthetic.tokens_device(T, mu, sg, kw.seed, sev)
+        packed.append(P.rptq_kv_quant_pack(x, dev(par[0]), par[1], par[2], par[3], bits))
+        raw.append(x)
+        params.append(par)
+    q = (np.random.default_rng(5).standard_normal((B, C)) * 0.25).astype(np.float16)
+    dp = lambda par: (dev(par[0]), par[1], par[2], par[3])
+    got = P.rptq_kv_attention(dev(q.view(np.int16)).view(torch.float16), packed[0], packed[1], B, Ts, C, D,
+                              float(1.0 / np.sqrt(D)), dp(params[0]), dp(params[1]), bits).cpu().numpy()
+    del packed
+    for b in (0, 41):
+        rows = slice(b * Ts, (b + 1) * Ts)
+        kp, vp = (orc.kv_quant_pack(r[rows].cpu().numpy().view(np.uint16), *par, bits)
+                  for r, par in zip(raw, params))
+        want = orc.kv_attention(q[b:b + 1], kp, vp, 1, Ts, C, D, 1.0 / np.sqrt(D), params[0], params[1], bits)
+        assert rel_l2(got[b], want[0]) <= 1e-3, (b, rel_l2(got[b], want[0]))

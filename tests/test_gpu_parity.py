@@ -271,6 +271,42 @@ def test_qgemm_quant_output(P, ab, wb, ob, act, N):
     assert d.max() <= 1 and (d > 0).mean() <= 1e-3, (d.max(), (d > 0).mean())
 
 
+# ----------------------------------------------------------------------------- attention over packed KV
+def _attn_inputs(B, T, C, g, bits, seed):
+    out = []
+    for k, (sch, scal, sev) in enumerate(((synthetic.STREAM_CHANNELS, synthetic.STREAM_CALIB, synthetic.STREAM_EVAL),
+                                          (synthetic.STREAM_CHANNELS_V, synthetic.STREAM_CALIB_V,
+                                           synthetic.STREAM_EVAL_V))):
+        mu, sg = synthetic.channel_params(C, seed, 0.01, stream=sch)
+        xc = synthetic.tokens(256, mu, sg, seed, scal)
+        mx, mn = orc.channel_minmax(xc)
+        R, bounds, s, z = orc.calibrate(mx, mn, g, bits, synthetic.kmeans_uniforms(seed + k, 2, g), n_init=2)
+        x = synthetic.tokens(B * T, mu, sg, seed, sev)
+        out.append((orc.kv_quant_pack(x, R, bounds, s, z, bits), (R, bounds, s, z)))
+    return out
+
+
+@pytest.mark.parametrize("B,T,C,D,g,bits", [(2, 300, 1024, 128, 8, 3), (3, 129, 512, 64, 4, 4),
+                                           (1, 1, 256, 128, 2, 8), (2, 1000, 9216, 128, 32, 3),
+                                           (5, 77, 640, 64, 5, 3)])
+def test_kv_attention_matches_oracle(P, B, T, C, D, g, bits):
+    """Decode attention reading the packed caches: per sequence within 1e-3
+    (relative L2, the fp32 tolerance used for Y) of the oracle's fp64
+    attention over the dequantized caches (ragged last chunk, T = 1, both
+    head sizes, 3/4/8 bits)."""
+    _say("kv attention", B, T, C, D, g, bits)
+    (kp, kpar), (vp, vpar) = _attn_inputs(B, T, C, g, bits, seed=T + C + bits)
+    q = (np.random.default_rng(T + C).standard_normal((B, C)) * 0.25).astype(np.float16)
+    scale = 1.0 / np.sqrt(D)
+    want = orc.kv_attention(q, kp, vp, B, T, C, D, scale, kpar, vpar, bits)
+    qd = dev(q.view(np.int16)).view(torch.float16)
+    dp = lambda par: (dev(par[0]), par[1], par[2], par[3])
+    got = P.rptq_kv_attention(qd, dev(kp), dev(vp), B, T, C, D, float(scale), dp(kpar), dp(vpar), bits)
+    got = got.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        assert rel_l2(got[b], want[b]) <= 1e-3, (b, rel_l2(got[b], want[b]))
+
+
 # ----------------------------------------------------------------------------- calibration
 def test_calib_minmax_matches_oracle(P):
     K = 1024

@@ -468,6 +468,46 @@ def test_weight_quantization_bounds(orc, wbits):
     assert (err <= s_w.astype(np.float64) / 2 * (1 + 1e-6)).all()
 
 
+# ----------------------------------------------------------------------------- KV attention
+def _attn_case(orc, B, T, C, bits, seed):
+    mu, sg = synthetic.channel_params(C, seed, 0.02)
+    kv = [synthetic.tokens(B * T, mu, sg, seed, st) for st in (synthetic.STREAM_EVAL, synthetic.STREAM_CALIB)]
+    params = []
+    for x in kv:
+        mx, mn = orc.channel_minmax(x)
+        R, bounds, s, z = orc.calibrate(mx, mn, 4, bits, synthetic.kmeans_uniforms(seed, 2, 4), n_init=2)
+        params.append((R, bounds, s, z))
+    packed = [orc.kv_quant_pack(x, *p, bits) for x, p in zip(kv, params)]
+    return packed, params
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_kv_attention_special_cases(orc, bits):
+    """Closed forms of softmax attention: a zero query weighs every token
+    equally (out = mean of the dequantized values); one cached token gives
+    its value row; a query aligned with one key and scaled up selects that
+    token's value row."""
+    B, T, C, D = 2, 6, 64, 16
+    (kp, vp), (kpar, vpar) = _attn_case(orc, B, T, C, bits, 41)
+    V = orc.half_to_double(orc.kv_dequant(vp, C, *vpar, bits)).reshape(B, T, C)
+    K = orc.half_to_double(orc.kv_dequant(kp, C, *kpar, bits)).reshape(B, T, C)
+    q0 = np.zeros((B, C), np.float16)
+    out = orc.kv_attention(q0, kp, vp, B, T, C, D, 0.25, kpar, vpar, bits)
+    np.testing.assert_allclose(out, V.mean(axis=1), rtol=1e-12, atol=1e-12)
+    out1 = orc.kv_attention(q0[:, :], kp.reshape(B, T, -1)[:, :1].reshape(B, -1),
+                            vp.reshape(B, T, -1)[:, :1].reshape(B, -1), B, 1, C, D, 0.25, kpar, vpar, bits)
+    np.testing.assert_allclose(out1, V[:, 0], rtol=0, atol=0)
+    # query = the key of token 3 (per head), with a large scale: softmax -> one-hot
+    qk = K[:, 3].astype(np.float16)
+    outk = orc.kv_attention(qk, kp, vp, B, T, C, D, 1e3, kpar, vpar, bits)
+    for b in range(B):
+        for h in range(C // D):
+            sl = slice(h * D, (h + 1) * D)
+            sc = K[b, :, sl] @ qk[b, sl].astype(np.float64)
+            if np.sort(sc)[-1] - np.sort(sc)[-2] > 0.05:        # a clear winner
+                np.testing.assert_allclose(outk[b, sl], V[b, int(np.argmax(sc)), sl], rtol=1e-6, atol=1e-6)
+
+
 # ----------------------------------------------------------------------------- KV cache
 @pytest.mark.parametrize("bits", [3, 4, 8])
 def test_kv_round_trip_error_and_natural_order(orc, bits):
