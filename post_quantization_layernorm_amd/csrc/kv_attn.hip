@@ -11,7 +11,8 @@
 //
 // One query token per sequence (decode).  Work is split flash-decoding
 // style: workgroup (b, k) handles tokens [k*TC, k*TC + TC) of sequence b in
-// three phases, all on one LDS row buffer:
+// three phases, the packed rows streaming through a ring of LDS slots
+// several rows ahead:
 //   1. scores: for each key row, LPH = D/16 lanes per head each take 16
 //      channels (packed-fp16 dot products), reduced with lane shuffles:
 //      S[t][h] = scale * q_h . k_h;
@@ -27,6 +28,24 @@ namespace {
 
 constexpr int kAttnBlock = 256;
 constexpr int kAttnMaxRounds = 4;          // score tasks per lane: H * D/16 <= 4 * 256
+constexpr int kAttnRing = 4;               // packed rows in flight per workgroup
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Wait until this wave has at most n vector-memory operations pending.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete, its memory loads may still be in flight (a full __syncthreads
+// would wait for the ring's prefetches too).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -34,11 +53,31 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Per code of the packed row (unit-major: code e of unit u at u * 8 + e):
+// its natural channel, and its cluster's s and z.
+struct AttnTable {
+    uint16_t* dst;
+    float* s;
+    float* z;
+};
+
+template <int BITS>
+__global__ __launch_bounds__(256) void kv_attn_tables_kernel(int32_t C, const int32_t* __restrict__ R,
+                                                             const ClusterArgs ca, AttnTable tb) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;       // unit * 8 + e
+    if (i >= C) return;
+    const int unit = i >> 3, e = i & 7;
+    const int j = UnitGeom<BITS>::first(unit) + e * UnitGeom<BITS>::stride;
+    const int c = cluster_of_pos(ca, j);
+    tb.dst[i] = (uint16_t)(R ? R[j] : j);
+    tb.s[i] = ca.s[c];
+    tb.z[i] = (float)ca.z[c];
+}
+
 template <int BITS, int UPL, int D>
 __global__ __launch_bounds__(kAttnBlock) void kv_attn_chunk_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kp, const uint8_t* __restrict__ vp,
-    int32_t T, int32_t C, int32_t TC, int32_t nch, float scale,
-    const int32_t* __restrict__ Rk, const ClusterArgs ck, const int32_t* __restrict__ Rv, const ClusterArgs cv,
+    int32_t T, int32_t C, int32_t TC, int32_t nch, float scale, const AttnTable tk, const AttnTable tv,
     float* __restrict__ o_part, float* __restrict__ ml) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int CH = chunks_for<true>(UPL * BITS);          // packed row: C*BITS/8 bytes
@@ -49,58 +88,114 @@ __global__ __launch_bounds__(kAttnBlock) void kv_attn_chunk_kernel(
     const int t0 = kc * TC;
     const int nv = min(TC, T - t0);                           // tokens of this chunk (>= 1)
     const int64_t row_bytes = (int64_t)C * BITS / 8;
-    unsigned char* prow = smem;                               // CH * 16 * block bytes
-    unsigned char* xrow = prow + (size_t)CH * 16 * kAttnBlock;   // UPL * 16 * block >= 2 C bytes
+    constexpr int SLOT = CH * 16 * kAttnBlock;                // one packed row
+    unsigned char* ring = smem;                               // kAttnRing slots
+    unsigned char* xrow = ring + (size_t)kAttnRing * SLOT;    // UPL * 16 * block >= 2 C bytes
     unsigned char* dummy = xrow + (size_t)UPL * 16 * kAttnBlock; // 16 bytes
     float* S = reinterpret_cast<float*>(dummy + 16);          // [TC][H]
     const int n_units = C / 8;
 
-    // per-lane units of 8 codes: destination channel, s and z of each code
+    // per-lane units of 8 codes: destination byte in xrow, s and z of each
+    // code, read from the tables kv_attn_tables_kernel built once per call
     int dst[UPL][8], uib[UPL];
     float sc[UPL][8], zf[UPL][8];
-    auto tables = [&](const int32_t* R, const ClusterArgs& ca) {
+    auto tables = [&](const AttnTable& tb) {
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
             const int unit = tid + u * kAttnBlock;
             const bool live = unit < n_units;
             uib[u] = live ? UnitGeom<BITS>::out_byte(unit) : 0;
+            const int uu = live ? unit : 0;
+            const u32x4 d4 = *reinterpret_cast<const u32x4*>(tb.dst + uu * 8);
+            const uint32_t dw[4] = {d4.x, d4.y, d4.z, d4.w};
+            const float4 s0 = reinterpret_cast<const float4*>(tb.s + uu * 8)[0];
+            const float4 s1 = reinterpret_cast<const float4*>(tb.s + uu * 8)[1];
+            const float4 z0 = reinterpret_cast<const float4*>(tb.z + uu * 8)[0];
+            const float4 z1 = reinterpret_cast<const float4*>(tb.z + uu * 8)[1];
+            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                dst[u][e] = (int)(dummy - xrow); sc[u][e] = 0.0f; zf[u][e] = 0.0f;
-                if (live) {
-                    const int j = UnitGeom<BITS>::first(unit) + e * UnitGeom<BITS>::stride;
-                    const int c = cluster_of_pos(ca, j);
-                    dst[u][e] = (R ? R[j] : j) * 2;
-                    sc[u][e] = ca.s[c];
-                    zf[u][e] = (float)ca.z[c];
-                }
+                dst[u][e] = live ? (int)((dw[e / 2] >> (16 * (e & 1))) & 0xFFFFu) * 2 : (int)(dummy - xrow);
+                sc[u][e] = sv[e];
+                zf[u][e] = zv[e];
             }
         }
     };
 
-    // Rows b*T + t0 .. + nv - 1 of one tensor: each is staged in LDS,
-    // dequantized into xrow (fp16, natural order) and handed to consume(t).
-    // The next row's load is in flight meanwhile; a load past the chunk uses
-    // a descriptor of size 0 (reads nothing), so no load is conditional.
-    u32x4 buf[CH];
+    // Rows b*T + t0 .. + nv - 1 of one tensor.  Packed rows travel straight
+    // from HBM into a ring of kAttnRing LDS slots (buffer loads that write
+    // LDS: lane l of a wave lands at the wave's base + 16 l, so a row keeps
+    // its byte order), kAttnRing rows ahead; each is dequantized into xrow
+    // (fp16, natural order) and handed to consume(t).  Every wave issues CH
+    // such loads per row, loads past the chunk use a descriptor of size 0,
+    // so the memory-counter waits are fixed counts.
+    auto issue_row = [&](const uint8_t* rows, int t) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(rows + (int64_t)t * row_bytes, t < nv ? row_bytes : 0);
+        unsigned char* slot = ring + (size_t)(t % kAttnRing) * SLOT;
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(slot + (size_t)(wv * 64 + i * kAttnBlock) * 16),
+                                                     16, (uint32_t)(tid + i * kAttnBlock) * 16u, 0, 0, 0);
+    };
     auto run_rows = [&](const uint8_t* base, auto&& consume) {
         const uint8_t* rows = base + ((int64_t)b * T + t0) * row_bytes;
-        load_row_chunks<true, CH>(buf, rows, row_bytes);
+        wait_vm<0>();                                         // nothing older in the count
+        __syncthreads();                                      // the ring is free
+#pragma unroll
+        for (int p = 0; p < kAttnRing; ++p) issue_row(rows, p);
         for (int t = 0; t < nv; ++t) {
-            put_row_chunks<true, CH>(prow, buf);
-            __syncthreads();                                  // prow ready; xrow free
-            load_row_chunks<true, CH>(buf, rows + (int64_t)(t + 1) * row_bytes, t + 1 < nv ? row_bytes : 0);
+            wait_vm<(kAttnRing - 1) * CH>();                  // this wave's part of row t is in LDS
+            lds_barrier();                                    // every part; xrow free
+            const unsigned char* prow = ring + (size_t)(t % kAttnRing) * SLOT;
+            // every unit's packed bytes first (their LDS reads overlap), then
+            // decode, dequantize and scatter
+            uint32_t raw[UPL][BITS == 8 ? 2 : BITS == 4 ? 1 : 3];
+#pragma unroll
+            for (int u = 0; u < UPL; ++u) {
+                const unsigned char* pu = prow + uib[u];
+                if constexpr (BITS == 8) {
+                    const uint2 v = *reinterpret_cast<const uint2*>(pu);
+                    raw[u][0] = v.x; raw[u][1] = v.y;
+                } else if constexpr (BITS == 4) {
+                    raw[u][0] = *reinterpret_cast<const uint32_t*>(pu);
+                } else {
+                    raw[u][0] = pu[0]; raw[u][1] = pu[4]; raw[u][2] = pu[8];
+                }
+            }
 #pragma unroll
             for (int u = 0; u < UPL; ++u) {
                 int qv[8];
-                load_unit_at<BITS>(prow + uib[u], qv);
+                if constexpr (BITS == 8) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        qv[i] = (raw[u][0] >> (8 * i)) & 255;
+                        qv[4 + i] = (raw[u][1] >> (8 * i)) & 255;
+                    }
+                } else if constexpr (BITS == 4) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        qv[i] = (raw[u][0] >> (8 * i)) & 15;
+                        qv[4 + i] = (raw[u][0] >> (8 * i + 4)) & 15;
+                    }
+                } else {
+                    // one byte of each of the group's three words (3-bit layout)
+                    const int b0 = raw[u][0], b1 = raw[u][1], b2 = raw[u][2];
+                    qv[0] = b0 & 7; qv[1] = (b0 >> 3) & 7;
+                    qv[2] = b1 & 7; qv[3] = (b1 >> 3) & 7;
+                    qv[4] = b2 & 7; qv[5] = (b2 >> 3) & 7;
+                    qv[6] = (b0 >> 6) | ((b2 >> 6) & 1) << 2;
+                    qv[7] = (b1 >> 6) | ((b2 >> 7) & 1) << 2;
+                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     *reinterpret_cast<_Float16*>(xrow + dst[u][e]) = (_Float16)(sc[u][e] * ((float)qv[e] - zf[u][e]));
             }
-            __syncthreads();                                  // xrow holds row t
+            lds_barrier();                                    // xrow holds row t; slot t free
+            issue_row(rows, t + kAttnRing);
             consume(t);
         }
+        wait_vm<0>();
         __syncthreads();
     };
 
@@ -118,7 +213,7 @@ __global__ __launch_bounds__(kAttnBlock) void kv_attn_chunk_kernel(
         qa[r][0] = on ? *reinterpret_cast<const u32x4*>(q + (int64_t)b * C + ch) : u32x4{0u, 0u, 0u, 0u};
         qa[r][1] = on ? *reinterpret_cast<const u32x4*>(q + (int64_t)b * C + ch + 8) : u32x4{0u, 0u, 0u, 0u};
     }
-    tables(Rk, ck);
+    tables(tk);
     run_rows(kp, [&](int t) {
 #pragma unroll
         for (int r = 0; r < kAttnMaxRounds; ++r) {
@@ -167,7 +262,7 @@ __global__ __launch_bounds__(kAttnBlock) void kv_attn_chunk_kernel(
     for (int u = 0; u < UPL; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
-    tables(Rv, cv);
+    tables(tv);
     run_rows(vp, [&](int t) {
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
@@ -236,19 +331,26 @@ const void* pick_attn(int bits, int upl, int D) {
 }  // namespace
 
 void kv_attention_geometry(int32_t T, int32_t C, int32_t D, int32_t& TC, int32_t& nch) {
-    // tokens per chunk: the score tile TC x H fp32 stays within 48 KB of LDS
+    // tokens per chunk: the score tile TC x H fp32 stays within 40 KB of LDS
+    // (two workgroups per CU with the row ring and the dequantized row)
     const int H = C / D;
     TC = 128;
-    while (TC > 1 && (int64_t)TC * H * 4 > 48 * 1024) TC >>= 1;
+    while (TC > 1 && (int64_t)TC * H * 4 > 40 * 1024) TC >>= 1;
     nch = (T + TC - 1) / TC;
 }
+
+// Workspace: per-chunk outputs [B][nch][C] fp32, softmax statistics
+// [B][nch][H][2] fp32, then the K and V code tables (C x (2 + 4 + 4) bytes
+// each); every part starts on a 256-byte boundary.
+static int64_t up256(int64_t n) { return (n + 255) / 256 * 256; }
 
 int64_t kv_attention_workspace(int32_t B, int32_t T, int32_t C, int32_t D) {
     int32_t TC = 0, nch = 0;
     kv_attention_geometry(T, C, D, TC, nch);
     const int64_t o_bytes = (int64_t)B * nch * C * 4;
     const int64_t ml_bytes = (int64_t)B * nch * (C / D) * 2 * 4;
-    return (o_bytes + 255) / 256 * 256 + ml_bytes;
+    const int64_t tab = up256((int64_t)C * 2) + 2 * up256((int64_t)C * 4);
+    return up256(o_bytes) + up256(ml_bytes) + 2 * tab;
 }
 
 hipError_t launch_kv_attention(const uint16_t* q, const uint8_t* kp, const uint8_t* vp, int32_t B, int32_t T,
@@ -264,16 +366,36 @@ hipError_t launch_kv_attention(const uint16_t* q, const uint8_t* kp, const uint8
     const void* k = pick_attn(ck.bits, upl, D);
     if (!k) return hipErrorInvalidValue;
     const int ch = chunks_for<true>(upl * ck.bits);
-    const size_t lds = (size_t)ch * 16 * block + (size_t)upl * 16 * block + 16 + (size_t)TC * (C / D) * 4;
+    const size_t lds = (size_t)kAttnRing * ch * 16 * block + (size_t)upl * 16 * block + 16 + (size_t)TC * (C / D) * 4;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    float* o_part = static_cast<float*>(workspace);
-    float* ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         ((int64_t)B * nch * C * 4 + 255) / 256 * 256);
+    char* w = static_cast<char*>(workspace);
+    float* o_part = reinterpret_cast<float*>(w);
+    w += up256((int64_t)B * nch * C * 4);
+    float* ml = reinterpret_cast<float*>(w);
+    w += up256((int64_t)B * nch * (C / D) * 2 * 4);
+    AttnTable tab[2];
+    for (int i = 0; i < 2; ++i) {
+        tab[i].dst = reinterpret_cast<uint16_t*>(w);
+        w += up256((int64_t)C * 2);
+        tab[i].s = reinterpret_cast<float*>(w);
+        w += up256((int64_t)C * 4);
+        tab[i].z = reinterpret_cast<float*>(w);
+        w += up256((int64_t)C * 4);
+    }
+    const void* tk = ck.bits == 3 ? (const void*)kv_attn_tables_kernel<3>
+                   : ck.bits == 4 ? (const void*)kv_attn_tables_kernel<4> : (const void*)kv_attn_tables_kernel<8>;
+    for (int i = 0; i < 2; ++i) {
+        const int32_t* R = i ? Rv : Rk;
+        const ClusterArgs& ca = i ? cv : ck;
+        void* targs[] = {(void*)&C, (void*)&R, (void*)&ca, (void*)&tab[i]};
+        hipError_t e = hipLaunchKernel(tk, dim3((unsigned)((C + 255) / 256)), dim3(256), targs, 0, stream);
+        if (e != hipSuccess) return e;
+    }
     void* args[] = {(void*)&q, (void*)&kp, (void*)&vp, (void*)&T, (void*)&C, (void*)&TC, (void*)&nch,
-                    (void*)&scale, (void*)&Rk, (void*)&ck, (void*)&Rv, (void*)&cv, (void*)&o_part, (void*)&ml};
+                    (void*)&scale, (void*)&tab[0], (void*)&tab[1], (void*)&o_part, (void*)&ml};
     hipError_t e = hipLaunchKernel(k, dim3((unsigned)(B * nch)), dim3(block), args, lds, stream);
     if (e != hipSuccess) return e;
     void* args2[] = {(void*)&o_part, (void*)&ml, (void*)&C, (void*)&D, (void*)&nch, (void*)&out};

@@ -192,7 +192,9 @@ def test_kv_attention_b0_noop_and_workspace_size(P):
     assert _attn(P, B=0, q=None, k=None, v=None, out=None, ws=None, wsz=0) == 0
     # 64 sequences x 8192 tokens, 9216 channels, head 128: 64 chunks of 128 tokens
     n = P.rptq_kv_attention_workspace_bytes(64, 8192, 9216, 128)
-    assert n == 64 * 64 * 9216 * 4 + 64 * 64 * 72 * 2 * 4
+    up = lambda v: (v + 255) // 256 * 256
+    # partial outputs, softmax statistics, then the K and V code tables
+    assert n == up(64 * 64 * 9216 * 4) + up(64 * 64 * 72 * 2 * 4) + 2 * (up(9216 * 2) + 2 * up(9216 * 4))
     assert P.rptq_kv_attention_workspace_bytes(1, 0, 256, 128) == -1
     assert P.rptq_kv_attention_workspace_bytes(1, 5, 256, 96) == -1
 
