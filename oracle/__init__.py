@@ -268,6 +268,31 @@ def ln_reorder_quant(x_f16, gamma, beta, eps, R, bounds, s, z, bits, return_y=Fa
     return (codes, y) if return_y else codes
 
 
+# ----------------------------------------------------------------------------- dynamic ranges
+def dynamic_cluster_params(y, bounds, bits):
+    """Dynamic ranges (quantization lecture 1.1: the scale is decided at run
+    time from the current activations).  The calibration rule applied to THIS
+    batch: per reordered position the (max, min) over the rows of y (fp32
+    [M][K], R order), then each cluster's (s, z) from them.  Returns (s, z)."""
+    mx, mn = channel_minmax(np.asarray(y, np.float32))
+    return cluster_params(mx, mn, None, bounds, bits)
+
+
+def quantize_dynamic(y, bounds, bits):
+    """Quantize-only mode with dynamic ranges: y fp32 [M][K] in R order.
+    Returns (SEG32 codes, s, z)."""
+    s, z = dynamic_cluster_params(y, bounds, bits)
+    return pack_seg32(quantize(y, bounds, s, z, bits), bounds, bits), s, z
+
+
+def ln_reorder_quant_dynamic(x_f16, gamma, beta, eps, R, bounds, bits, return_y=False):
+    """Reordered LayerNorm, then dynamic (s, z) from this batch's y, then the
+    per-cluster quantization and SEG32 pack.  Returns (codes, s, z[, y])."""
+    y = layernorm(x_f16, gamma, beta, eps, R)
+    codes, s, z = quantize_dynamic(y, bounds, bits)
+    return (codes, s, z, y) if return_y else (codes, s, z)
+
+
 # ----------------------------------------------------------------------------- weights / GEMM
 def quantize_weights(W, wbits):
     W = _c(W, np.float32); K, N = W.shape

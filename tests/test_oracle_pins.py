@@ -532,3 +532,91 @@ def test_kv_round_trip_error_and_natural_order(orc, bits):
     q = orc.unpack_dense(packed, C, bits)
     q2 = orc.quantize(np.ascontiguousarray(kv[:, R].astype(np.float32)), bounds, s, z, bits)
     assert np.array_equal(q, q2)
+
+
+# ----------------------------------------------------------------------------- dynamic ranges
+def test_dynamic_ranges_hand_worked_example(orc):
+    # quantization lecture 1.1 (dynamic: the scale comes from the current
+    # activations) with 1.3's asymmetric s, z.  Two clusters of two channels,
+    # two rows, 4 bits (qmax 15), worked by hand:
+    #   cluster 0: values -1, 0.5, 2, 0 -> lo -1, hi 2, s = fp32(3/15) = fp32(0.2),
+    #              z = rne(1/s) = 5 (1/s = 4.99999993), 1/s in fp32 = 5.0:
+    #              -1 -> -5+5 = 0, 0.5 -> rne(2.5) = 2 -> 7, 2 -> 15, 0 -> 5
+    #   cluster 1: values 3, 4, 5, 3.5 (range excludes 0) -> lo 3, hi 5,
+    #              s = fp32(2/15), z = rne(-3/s) = rne(-22.4999994) = -22,
+    #              1/s in fp32 = 7.4999995: 3 -> 22 -> 0, 4 -> 30 -> 8,
+    #              5 -> 37 -> 15, 3.5 -> 26 -> 4
+    y = np.array([[-1.0, 0.5, 3.0, 4.0], [2.0, 0.0, 5.0, 3.5]], np.float32)
+    b = np.array([0, 2, 4], np.int32)
+    s, z = orc.dynamic_cluster_params(y, b, 4)
+    assert s[0] == np.float32(0.2) and s[1] == np.float32(2.0 / 15.0)
+    assert z.tolist() == [5, -22]
+    codes, s2, z2 = orc.quantize_dynamic(y, b, 4)
+    q = orc.unpack_seg32(codes, 4, b, 4)
+    assert q.tolist() == [[0, 7, 0, 8], [15, 5, 15, 4]]
+    assert np.array_equal(s, s2) and np.array_equal(z, z2)
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_dynamic_ranges_cover_the_batch(orc, bits):
+    # every value lies inside its cluster's own range, so (up to rounding at
+    # the two ends) nothing is clipped: the smallest code of each cluster is 0
+    # or 1, the largest qmax - 1 or qmax, and every value dequantizes within
+    # one step; the extremes sit in rows other than the first (a range taken
+    # from one row, or one range per channel, fails these)
+    r = np.random.default_rng(31 + bits)
+    M, K, g = 48, 160, 5
+    b = np.array([0, 8, 40, 72, 130, 160], np.int32)
+    y = (r.standard_normal((M, K)) * r.uniform(0.1, 6.0, K)).astype(np.float32)
+    y[:, 40:72] += np.float32(9.0)               # a cluster whose range excludes 0
+    y[M - 1, 3] = np.float32(50.0)               # extremes in the last rows
+    y[M - 2, 100] = np.float32(-70.0)
+    qmax = (1 << bits) - 1
+    codes, s, z = orc.quantize_dynamic(y, b, bits)
+    q = orc.unpack_seg32(codes, K, b, bits).astype(np.int64)
+    for c in range(g):
+        qc = q[:, b[c]:b[c + 1]]
+        yc = y[:, b[c]:b[c + 1]].astype(np.float64)
+        assert qc.min() in (0, 1) and qc.max() in (qmax - 1, qmax), (c, qc.min(), qc.max())
+        deq = float(s[c]) * (qc - int(z[c]))
+        assert np.abs(deq - yc).max() <= float(s[c]) * 1.0001
+        # the step follows the batch's own range
+        assert abs(float(s[c]) * qmax - (yc.max() - yc.min())) <= 1e-6 * (yc.max() - yc.min())
+    assert q[M - 1, 3] == qmax and q[M - 2, 100] == 0
+
+
+def test_dynamic_ranges_power_of_two_equivariance(orc):
+    # scaling the batch by 2^k scales every s by 2^k exactly and keeps z and
+    # the codes (all fp32 steps are exact under a power-of-two scaling)
+    r = np.random.default_rng(5)
+    y = (r.standard_normal((20, 96)) * 2.0 + 0.7).astype(np.float32)
+    b = np.array([0, 30, 64, 96], np.int32)
+    c1, s1, z1 = orc.quantize_dynamic(y, b, 4)
+    c2, s2, z2 = orc.quantize_dynamic(y * np.float32(8.0), b, 4)
+    assert np.array_equal(s2, s1 * np.float32(8.0))
+    assert np.array_equal(z1, z2) and np.array_equal(c1, c2)
+
+
+def test_dynamic_ln_matches_static_with_its_own_ranges(orc):
+    # the dynamic LayerNorm path is the static one with (s, z) calibrated on
+    # the same batch, and its ranges are those of the normalized rows
+    r = np.random.default_rng(9)
+    M, K = 24, 128
+    x = orc.float_to_half_bits((r.standard_normal((M, K)) * 2.0 + 0.3).astype(np.float32))
+    gamma = r.uniform(0.5, 1.5, K).astype(np.float32)
+    beta = (r.standard_normal(K) * 0.1).astype(np.float32)
+    R = r.permutation(K).astype(np.int32)
+    b = np.array([0, 17, 64, 100, 128], np.int32)
+    codes, s, z, y = orc.ln_reorder_quant_dynamic(x, gamma, beta, 1e-5, R, b, 4, return_y=True)
+    codes_static = orc.ln_reorder_quant(x, gamma, beta, 1e-5, R, b, s, z, 4)
+    assert np.array_equal(codes, codes_static)
+    # with gamma = 1, beta = 0 every row of the normalized output has mean 0
+    # and (biased) variance var / (var + eps), about 1 here
+    y1 = orc.layernorm(x, np.ones(K, np.float32), np.zeros(K, np.float32), 1e-5, R)
+    assert np.abs(y1.astype(np.float64).mean(axis=1)).max() < 1e-5
+    assert np.abs(y1.astype(np.float64).var(axis=1) - 1.0).max() < 1e-4
+    lo = [y[:, b[c]:b[c + 1]].min() for c in range(4)]
+    q = orc.unpack_seg32(codes, K, b, 4)
+    for c in range(4):
+        j = np.argwhere(y[:, b[c]:b[c + 1]] == lo[c])[0]
+        assert q[j[0], b[c] + j[1]] in (0, 1)
