@@ -136,6 +136,9 @@ def main():
         variants[ab] = dict(s=s, z=z, codes=torch.empty((M, rb), dtype=torch.uint8, device=dev))
     Y = torch.empty((M, N), dtype=torch.float32, device=dev)
     kpad = P.rptq_codes_kpad(bounds)
+    # dynamic ranges: (s, z) of the 4-bit clusters from each batch, on the device
+    dyn = dict(s=torch.empty(g, dtype=torch.float32, device=dev), z=torch.empty(g, dtype=torch.int32, device=dev),
+               codes=torch.empty((M, P.rptq_codes_row_bytes(bounds, 4)), dtype=torch.uint8, device=dev))
     log(f"[bench] weights ready, K_pad={kpad} ({time.time() - t_setup:.1f}s)")
 
     # fc1 with its output quantized for fc2 (ReLU, then fc2's 4-bit clusters):
@@ -187,7 +190,8 @@ def main():
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ one step
-    names = ["ln4", "gemm4", "ln3", "gemm3", "gemm3w3", "gemm4q", "kvq_K", "kvq_V", "kvd_K", "kvd_V", "kv_attn"]
+    names = ["ln4", "gemm4", "ln3", "gemm3", "gemm3w3", "gemm4q", "ln4d", "gemm4d", "kvq_K", "kvq_V", "kvd_K",
+             "kvd_V", "kv_attn"]
 
     def step(ev=None):
         def rec(i):
@@ -215,6 +219,17 @@ def main():
         P.rptq_qgemm_quant(v["codes"], M, K, qout["n_pad"], bounds, v["s"], v["z"], 4, qout["w"], w.w_bits,
                            qout["sw"], qout["cs"], P.RPTQ_ACT_RELU, qout["bounds"], qout["s"], qout["z"], 4,
                            out=qout["codes"], stream=stream)
+        k += 1
+        rec(k)
+        # the same layer with dynamic ranges (ranges pass + quantizing pass,
+        # then the GEMM reading (s, z) from device memory)
+        P.rptq_ln_reorder_quant_dynamic(x, R_d, gr_d, br_d, bounds, 4, out=dyn["codes"], s_out=dyn["s"],
+                                        z_out=dyn["z"], stream=stream)
+        k += 1
+        rec(k)
+        wp_d, cs_d, sw_d = wts[w.w_bits]
+        P.rptq_qgemm_dynamic(dyn["codes"], M, K, N, bounds, dyn["s"], dyn["z"], 4, wp_d, w.w_bits, sw_d, cs_d,
+                             out=Y, stream=stream)
         k += 1
         rec(k)
         for name in ("K", "V"):
@@ -287,7 +302,7 @@ def main():
                 "kernel": "qgemm_kernel<4,4>", "work_per_launch": f"2*M*N*K = {ops:.4g} int8 ops (unpadded K)"}
     ln_bytes = M * K * (2 + 4 / 8)
     rooflines = [roofline,
-                 {"bound": "hbm", "kernel": "ln_reorder_quant_kernel<4,0>", "achieved": ln_bytes / avg["ln4"] / 1e9,
+                 {"bound": "hbm", "kernel": "ln_reorder_quant_kernel<4,0,5,0>", "achieved": ln_bytes / avg["ln4"] / 1e9,
                   "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ln_bytes / avg["ln4"] / 1e9 / HBM_PEAK_GBPS,
                   "traffic": measured_traffic("ln_reorder_quant", ln_bytes)}]
     rooflines.append({"bound": "hbm", "kernel": "kv_quant_pack_kernel<3>", "achieved": out["kv_pack_GBps"],
@@ -322,6 +337,12 @@ def main():
         "w4a4_quant_out": {"gemm_ms": avg["gemm4q"] * 1e3, "gemm_tops": ops / avg["gemm4q"] / 1e12,
                            "gemm_frac_int8_peak": ops / avg["gemm4q"] / 1e12 / INT8_PEAK_TOPS,
                            "n_pad": n_pad, "out": "ReLU, fc2's 4-bit per-cluster codes (SEG32)"},
+        "w4a4_dynamic": {"ln_ms": avg["ln4d"] * 1e3, "gemm_ms": avg["gemm4d"] * 1e3,
+                         "tokens_per_s": M / (avg["ln4d"] + avg["gemm4d"]),
+                         "ln_GBps_two_reads": M * K * (4 + 4 / 8) / avg["ln4d"] / 1e9,
+                         "ln_frac_hbm_peak_two_reads": M * K * (4 + 4 / 8) / avg["ln4d"] / 1e9 / HBM_PEAK_GBPS,
+                         "gemm_tops": ops / avg["gemm4d"] / 1e12,
+                         "ln": "4 launches: (lo, hi) init, ranges pass over x, (s, z), quantizing pass"},
         "w3a3": {"gemm_ms": avg["gemm3w3"] * 1e3, "gemm_tops": ops / avg["gemm3w3"] / 1e12,
                  "gemm_frac_int8_peak": ops / avg["gemm3w3"] / 1e12 / INT8_PEAK_TOPS,
                  "tokens_per_s": M / (avg["ln3"] + avg["gemm3w3"])},
@@ -346,13 +367,14 @@ def main():
 # Kernels whose HBM traffic bench.py reports, matched on rocprofv3's kernel
 # names (pattern, which matching dispatch of the one-step counter run: an
 # index in dispatch order, or None for the mean of all): the W4A4 GEMM (the
-# step's first 4-4 GEMM; the last is fc1 with its output quantized for fc2),
-# the 4-bit fused LayerNorm-quant (the step's, after the calibration one), the
-# 3-bit KV pack (K and V).
+# step's 4-4 GEMMs are, in order, the plain one, fc1 with its output quantized
+# for fc2, and the dynamic-range one), the 4-bit fused LayerNorm-quant with
+# calibrated ranges (5 units per lane at K = 9216; the step's, after the
+# calibration one), the 3-bit KV pack (K and V).
 PMC_KERNELS = {
-    "qgemm": ("qgemm_kernel<4, 4, false", -2),
-    "qgemm_quant_out": ("qgemm_kernel<4, 4, false", -1),
-    "ln_reorder_quant": ("ln_reorder_quant_kernel<4, 0,", -1),
+    "qgemm": ("qgemm_kernel<4, 4, false", -3),
+    "qgemm_quant_out": ("qgemm_kernel<4, 4, false", -2),
+    "ln_reorder_quant": ("ln_reorder_quant_kernel<4, 0, 5, 0>", -1),
     "kv_quant_pack": ("kv_quant_pack_kernel<3,", None),
 }
 COPY_PROBE_BYTES = 1 << 30

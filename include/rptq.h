@@ -184,6 +184,47 @@ int rptq_qgemm_quant(const uint8_t* codes, int64_t M, int32_t K, int32_t N_pad,
                      const int32_t* out_z, int32_t out_bits, uint8_t* out_codes, float* Y, void* stream);
 
 /*
+ * Dynamic-range variant of rptq_ln_reorder_quant (quantization lecture 1.1:
+ * a dynamic scheme decides the scale at run time from the current
+ * activations instead of from offline profiling).  The calibrated R and
+ * cluster bounds are kept; each cluster's (s, z) is computed from THIS
+ * batch's values with the calibration rule of rptq_cluster_params:
+ *   lo_c = min over rows m and positions j of cluster c of y[m][j]
+ *   hi_c = max of the same values
+ *   s_c  = fp32((hi_c - lo_c) / qmax), at least max(|lo_c|, |hi_c|) * 2^-21,
+ *          1 if zero;  z_c = rne(-lo_c / s_c)
+ * with y as rptq_ln_reorder_quant defines it for in_mode, and then the codes
+ * are that function's codes with these (s, z) (no value is clipped beyond
+ * rounding, since every value lies inside its cluster's range).
+ * Four launches in stream order: (lo, hi) init, a ranges pass over x
+ * (float atomics per cluster), the (s, z) step, the quantizing pass; x is
+ * read twice.
+ * s_out    device fp32 [g]: receives s (used as scratch during the call).
+ * z_out    device int32 [g]: receives z (likewise).
+ * M >= 1 (ranges of no rows are undefined: RPTQ_ERR_INVALID_ARG).  Other
+ * arguments, limits and errors as rptq_ln_reorder_quant, without s and z.
+ * Magnitudes below about 2^-100 are outside the supported range (1/s must
+ * be a finite fp32).
+ */
+int rptq_ln_reorder_quant_dynamic(const void* x, int32_t in_mode, int64_t M, int32_t K,
+                                  const float* gamma_r, const float* beta_r, float eps,
+                                  const int32_t* R, const int32_t* bounds, int32_t g, int32_t bits,
+                                  uint8_t* codes, float* s_out, int32_t* z_out, void* stream);
+
+/*
+ * rptq_qgemm with the activation clusters' (s, z) in DEVICE memory (s_dev
+ * fp32 [g], z_dev int32 [g], e.g. the outputs of
+ * rptq_ln_reorder_quant_dynamic), so no host round trip sits between the
+ * dynamic ranges and the GEMM.  The result is rptq_qgemm's for the same
+ * values of (s, z), bit for bit.  No acc_debug output.  Other arguments,
+ * limits and errors as rptq_qgemm.
+ */
+int rptq_qgemm_dynamic(const uint8_t* codes, int64_t M, int32_t K, int32_t N,
+                       const int32_t* bounds, int32_t g, const float* s_dev, const int32_t* z_dev,
+                       int32_t a_bits, const uint8_t* w_packed, int32_t w_bits, const float* s_w,
+                       const int32_t* colsum, float* Y, void* stream);
+
+/*
  * K/V-cache quantize + pack (RPTQ write-up, evaluation: the KV-cache settings
  * W4A4KV / W4A3KV / W3A3KV quantize the key and value caches, which hold most
  * of the memory at large batch x sequence length).  Streaming, one pass.

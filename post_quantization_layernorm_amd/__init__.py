@@ -35,7 +35,8 @@ RPTQ_MAX_CLUSTERS = 64
 RPTQ_MAX_K = 16384
 
 EXPORTED = [
-    "rptq_ln_reorder_quant", "rptq_qgemm", "rptq_qgemm_quant", "rptq_kv_quant_pack", "rptq_kv_dequant",
+    "rptq_ln_reorder_quant", "rptq_ln_reorder_quant_dynamic", "rptq_qgemm", "rptq_qgemm_dynamic",
+    "rptq_qgemm_quant", "rptq_kv_quant_pack", "rptq_kv_dequant",
     "rptq_kv_attention", "rptq_kv_attention_workspace_bytes",
     "rptq_calib_minmax", "rptq_kmeans_reorder", "rptq_cluster_params", "rptq_quantize_weights",
     "rptq_pack_weights", "rptq_pack_weights_out", "rptq_codes_kpad", "rptq_codes_row_bytes", "rptq_weights_row_bytes",
@@ -71,7 +72,11 @@ def lib() -> ctypes.CDLL:
         sig = {
             "rptq_ln_reorder_quant": (_I32, [_P, _I32, _I64, _I32, _P, _P, ctypes.c_float, _P, _P, _I32,
                                              _P, _P, _I32, _P, _P]),
+            "rptq_ln_reorder_quant_dynamic": (_I32, [_P, _I32, _I64, _I32, _P, _P, ctypes.c_float, _P, _P,
+                                                     _I32, _I32, _P, _P, _P, _P]),
             "rptq_qgemm": (_I32, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
+            "rptq_qgemm_dynamic": (_I32, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _P,
+                                          _P]),
             "rptq_qgemm_quant": (_I32, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _I32,
                                         _P, _I32, _P, _P, _I32, _P, _P, _P]),
             "rptq_kv_quant_pack": (_I32, [_P, _I64, _I32, _P, _P, _I32, _P, _P, _I32, _P, _P]),
@@ -173,6 +178,40 @@ def rptq_ln_reorder_quant(x, R, gamma_r, beta_r, bounds, s, z, bits, eps=1e-5,
     st = lib().rptq_ln_reorder_quant(_dp(x), in_mode, M, K, _dp(gamma_r), _dp(beta_r), eps, _dp(R),
                                      _hp(b), b.size - 1, _hp(sh), _hp(zh), bits, _dp(out), _stream(stream))
     _check(st, "rptq_ln_reorder_quant")
+    return out
+
+
+def rptq_ln_reorder_quant_dynamic(x, R, gamma_r, beta_r, bounds, bits, eps=1e-5,
+                                  in_mode=RPTQ_IN_FP16_RAW, out=None, s_out=None, z_out=None, stream=None):
+    """Dynamic ranges: the clusters' (s, z) come from this batch.  Returns
+    (codes cuda uint8 [M][row_bytes], s cuda fp32 [g], z cuda int32 [g])."""
+    M, K = x.shape
+    b = _h(bounds, np.int32); g = b.size - 1
+    rb = rptq_codes_row_bytes(b, bits)
+    if rb < 0:
+        _check(RPTQ_ERR_INVALID_ARG, "rptq_codes_row_bytes")
+    if out is None:
+        out = torch.empty((M, rb), dtype=torch.uint8, device=x.device)
+    if s_out is None:
+        s_out = torch.empty(max(g, 1), dtype=torch.float32, device=x.device)
+    if z_out is None:
+        z_out = torch.empty(max(g, 1), dtype=torch.int32, device=x.device)
+    st = lib().rptq_ln_reorder_quant_dynamic(_dp(x), in_mode, M, K, _dp(gamma_r), _dp(beta_r), eps, _dp(R),
+                                             _hp(b), g, bits, _dp(out), _dp(s_out), _dp(z_out),
+                                             _stream(stream))
+    _check(st, "rptq_ln_reorder_quant_dynamic")
+    return out, s_out, z_out
+
+
+def rptq_qgemm_dynamic(codes, M, K, N, bounds, s_dev, z_dev, a_bits, w_packed, w_bits, s_w, colsum, out=None,
+                       stream=None):
+    """rptq_qgemm with (s, z) as cuda tensors (fp32 [g], int32 [g])."""
+    b = _h(bounds, np.int32)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    st = lib().rptq_qgemm_dynamic(_dp(codes), M, K, N, _hp(b), b.size - 1, _dp(s_dev), _dp(z_dev), a_bits,
+                                  _dp(w_packed), w_bits, _dp(s_w), _dp(colsum), _dp(out), _stream(stream))
+    _check(st, "rptq_qgemm_dynamic")
     return out
 
 

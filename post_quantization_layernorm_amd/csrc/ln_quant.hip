@@ -40,11 +40,45 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
     return t;
 }
 
-template <int BITS, int MODE, int UPL>
+// Dynamic ranges (quantization lecture 1.1: the scale is decided at run time
+// from the current activations): cluster c's (s, z) from lo = min, hi = max
+// of the batch's values over the cluster's channels, by the same rules as the
+// calibrated parameters (s = (hi - lo)/qmax in fp32, floored at
+// max(|lo|, |hi|) 2^-21, 1 for an all-zero cluster; z = rne(-lo/s)).
+// float max / min by integer atomics: for IEEE floats (no -0), signed-integer
+// order matches float order on non-negative values and reversed
+// unsigned-integer order matches it on negative ones
+__device__ __forceinline__ void atomic_fmax(float* addr, float v) {
+    if (v >= 0.0f) atomicMax(reinterpret_cast<int*>(addr), __builtin_bit_cast(int, v));
+    else atomicMin(reinterpret_cast<unsigned int*>(addr), __builtin_bit_cast(unsigned int, v));
+}
+__device__ __forceinline__ void atomic_fmin(float* addr, float v) {
+    if (v >= 0.0f) atomicMin(reinterpret_cast<int*>(addr), __builtin_bit_cast(int, v));
+    else atomicMax(reinterpret_cast<unsigned int*>(addr), __builtin_bit_cast(unsigned int, v));
+}
+
+__device__ __forceinline__ void dynamic_params(float lo, float hi, int qmax, float& s, int32_t& z) {
+    const double dlo = lo, dhi = hi;
+    float sc = (float)((dhi - dlo) / (double)qmax);
+    const float fl = (float)(__builtin_fmax(__builtin_fabs(dlo), __builtin_fabs(dhi)) * 0x1p-21);
+    if (sc < fl) sc = fl;
+    if (sc == 0.0f) sc = 1.0f;
+    s = sc;
+    z = (int32_t)__builtin_rint(-dlo / (double)sc);
+}
+
+// DM (dynamic mode): kStatic quantizes with the (s, z) of the cluster table;
+// kRanges only merges every cluster's min / max over the rows into
+// dyn_lo / dyn_hi (float atomics; no codes written); kDevParams quantizes
+// with the (s, z) found in dyn_s / dyn_z (device memory).
+enum { kStatic = 0, kRanges = 1, kDevParams = 2 };
+
+template <int BITS, int MODE, int UPL, int DM>
 __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
     const void* __restrict__ xin, int64_t M, int32_t K, int64_t row_bytes,
     const float* __restrict__ gamma_r, const float* __restrict__ beta_r, float eps,
-    const int32_t* __restrict__ R, const ClusterArgs ca, uint8_t* __restrict__ codes) {
+    const int32_t* __restrict__ R, const ClusterArgs ca, uint8_t* __restrict__ codes,
+    float* __restrict__ dyn_a, int32_t* __restrict__ dyn_b) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int QMAX = (1 << BITS) - 1;
     constexpr bool LN = MODE == RPTQ_IN_FP16_RAW;
@@ -62,6 +96,9 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
     unsigned char* orow = smem + (size_t)CH * 16 * BLOCK;
     unsigned char* dummy = orow + (size_t)OCH * 16 * BLOCK;
     float* red = reinterpret_cast<float*>(dummy + 16);
+    // ranges: per 32-code group (lo, hi)
+    float* glo = red + 64;
+    float* ghi = glo + ca.K_pad / 32;
     const int tid = threadIdx.x;
     const int n_units = ca.K_pad / 8;
     const int nchunks = row_in_bytes / 16;
@@ -87,8 +124,13 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
             const int p0 = UnitGeom<BITS>::first(unit);
             const int c = cluster_of_padded(ca, p0);
             const int n_c = ca.bounds[c + 1] - ca.bounds[c];
-            uinv[u] = ca.inv_s[c];
-            uzf[u] = (float)ca.z[c];               // |z| <= 2^21: exact
+            if constexpr (DM == kDevParams) {
+                uinv[u] = 1.0f / dyn_a[c];           // correctly rounded, as on the host
+                uzf[u] = (float)dyn_b[c];
+            } else {
+                uinv[u] = ca.inv_s[c];
+                uzf[u] = (float)ca.z[c];           // |z| <= 2^21: exact
+            }
             uob[u] = UnitGeom<BITS>::out_byte(unit);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -109,6 +151,9 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
         }
     }
     const float qhi = kRoundMagic + (float)QMAX;
+    [[maybe_unused]] float ulo[UPL], uhi[UPL];
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) { ulo[u] = __builtin_inff(); uhi[u] = -__builtin_inff(); }
 
     // Two register buffers: while row r (in one) is processed, rows r + G and
     // r + 2G are in flight (G = gridDim.x).  Rows at or past M are read as
@@ -183,27 +228,46 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
         load_row(buf, row + 2 * (int64_t)gridDim.x);
 
         const float nmr = -mean * rstd;
-#pragma unroll
-        for (int u = 0; u < UPL; ++u) {
-            uint32_t qb[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float y;
-                if constexpr (LN) {
-                    const float xv = (float)*reinterpret_cast<const _Float16*>(xrow + src[u][e]);
-                    const float n = __builtin_fmaf(xv, rstd, nmr);
-                    y = __builtin_fmaf(gam[u][e], n, bet[u][e]);
-                } else {
-                    y = __builtin_fmaf(gam[u][e], *reinterpret_cast<const float*>(xrow + src[u][e]), bet[u][e]);
-                }
-                qb[e] = quant_bits(y, uinv[u], uzf[u], qhi);
+        auto y_of = [&](int u, int e) {
+            if constexpr (LN) {
+                const float xv = (float)*reinterpret_cast<const _Float16*>(xrow + src[u][e]);
+                const float n = __builtin_fmaf(xv, rstd, nmr);
+                return __builtin_fmaf(gam[u][e], n, bet[u][e]);
+            } else {
+                return __builtin_fmaf(gam[u][e], *reinterpret_cast<const float*>(xrow + src[u][e]), bet[u][e]);
             }
-            store_unit_bits<BITS>(orow + uob[u], qb);
+        };
+        if constexpr (DM == kRanges) {
+            // running (lo, hi) of every unit over the rows, padding
+            // positions (beta kPad) left out; rows past M add nothing
+            if (row < M) {
+#pragma unroll
+                for (int u = 0; u < UPL; ++u)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float y = y_of(u, e);
+                        const bool pad = bet[u][e] == kPad;
+                        ulo[u] = __builtin_fminf(ulo[u], pad ? __builtin_inff() : y);
+                        uhi[u] = __builtin_fmaxf(uhi[u], pad ? -__builtin_inff() : y);
+                    }
+            }
+            __syncthreads();          // every lane is done with the row and the sums
+            return;
+        } else {
+#pragma unroll
+            for (int u = 0; u < UPL; ++u) {
+                uint32_t qb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qb[e] = quant_bits(y_of(u, e), uinv[u], uzf[u], qhi);
+                store_unit_bits<BITS>(orow + uob[u], qb);
+            }
         }
-        __syncthreads();
-        // 3-bit rows are a multiple of 12 bytes: 4-byte stores
-        store_row_chunks<BITS != 3, chunks_for<BITS != 3>(UPL * BITS)>(codes + row * row_bytes,
-                                                                       row < M ? row_bytes : 0, orow);
+        if constexpr (DM != kRanges) {
+            __syncthreads();
+            // 3-bit rows are a multiple of 12 bytes: 4-byte stores
+            store_row_chunks<BITS != 3, chunks_for<BITS != 3>(UPL * BITS)>(codes + row * row_bytes,
+                                                                           row < M ? row_bytes : 0, orow);
+        }
     };
 
     const int64_t G = gridDim.x;
@@ -217,18 +281,114 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
         process(bufA, row);
         process(bufB, row + G);
     }
+
+    if constexpr (DM == kRanges) {
+        // units -> 32-code groups (4 consecutive units in 4 consecutive
+        // lanes) -> clusters (one wave per cluster at a time) -> device
+        // (lo, hi) by float atomics
+#pragma unroll
+        for (int u = 0; u < UPL; ++u) {
+            float lo = ulo[u], hi = uhi[u];
+            lo = __builtin_fminf(lo, __shfl_xor(lo, 1, 64));
+            hi = __builtin_fmaxf(hi, __shfl_xor(hi, 1, 64));
+            lo = __builtin_fminf(lo, __shfl_xor(lo, 2, 64));
+            hi = __builtin_fmaxf(hi, __shfl_xor(hi, 2, 64));
+            const int unit = tid + u * BLOCK;
+            if ((tid & 3) == 0 && unit < n_units) {
+                glo[unit >> 2] = lo;
+                ghi[unit >> 2] = hi;
+            }
+        }
+        __syncthreads();
+        for (int c = wv; c < ca.g; c += nw) {
+            float lo = __builtin_inff(), hi = -__builtin_inff();
+            for (int q = ca.off[c] / 32 + lane; q < ca.off[c + 1] / 32; q += 64) {
+                lo = __builtin_fminf(lo, glo[q]);
+                hi = __builtin_fmaxf(hi, ghi[q]);
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                lo = __builtin_fminf(lo, __shfl_xor(lo, o, 64));
+                hi = __builtin_fmaxf(hi, __shfl_xor(hi, o, 64));
+            }
+            // a workgroup without rows keeps (+inf, -inf): nothing to merge
+            if (lane == 0 && lo <= hi) {
+                atomic_fmin(reinterpret_cast<float*>(dyn_b) + c, lo + 0.0f);
+                atomic_fmax(dyn_a + c, hi + 0.0f);
+            }
+        }
+    }
 }
 
-template <int BITS, int MODE>
+// Cluster (s, z) from the merged (lo, hi), in place: dyn_a[c] holds hi and
+// becomes s, dyn_b[c] holds lo (as float bits) and becomes z.
+template <int BITS>
+__global__ void dynamic_params_kernel(float* __restrict__ dyn_a, int32_t* __restrict__ dyn_b, int32_t g) {
+    const int c = threadIdx.x;
+    if (c >= g) return;
+    const float hi = dyn_a[c], lo = __builtin_bit_cast(float, dyn_b[c]);
+    float sc;
+    int32_t zc;
+    dynamic_params(lo, hi, (1 << BITS) - 1, sc, zc);
+    dyn_a[c] = sc;
+    dyn_b[c] = zc;
+}
+
+__global__ void dynamic_init_kernel(float* __restrict__ dyn_a, int32_t* __restrict__ dyn_b, int32_t g) {
+    const int c = threadIdx.x;
+    if (c < g) {
+        dyn_a[c] = -__builtin_inff();
+        dyn_b[c] = __builtin_bit_cast(int32_t, __builtin_inff());
+    }
+}
+
+template <int BITS, int MODE, int DM>
 const void* pick(int upl) {
     switch (upl) {
-        case 1: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 1>;
-        case 2: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 2>;
-        case 3: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 3>;
-        case 4: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 4>;
-        case 5: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 5>;
+        case 1: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 1, DM>;
+        case 2: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 2, DM>;
+        case 3: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 3, DM>;
+        case 4: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 4, DM>;
+        case 5: return (const void*)ln_reorder_quant_kernel<BITS, MODE, 5, DM>;
         default: return nullptr;
     }
+}
+
+template <int DM>
+const void* pick_mode(int in_mode, int bits, int upl) {
+    if (in_mode == RPTQ_IN_FP16_RAW)
+        return bits == 3 ? pick<3, 0, DM>(upl) : bits == 4 ? pick<4, 0, DM>(upl) : pick<8, 0, DM>(upl);
+    return bits == 3 ? pick<3, 1, DM>(upl) : bits == 4 ? pick<4, 1, DM>(upl) : pick<8, 1, DM>(upl);
+}
+
+}  // namespace
+
+namespace {
+
+hipError_t launch_mode(int dm, const void* x, int in_mode, int64_t M, int32_t K, const float* gamma_r,
+                       const float* beta_r, float eps, const int32_t* R, const ClusterArgs& ca,
+                       int64_t row_bytes, uint8_t* codes, float* dyn_a, int32_t* dyn_b, hipStream_t stream) {
+    int upl = 0, block = 0;
+    unit_split(ca.K_pad / 8, upl, block, RPTQ_LN_MAX_BLOCK);
+    const void* k = dm == kRanges ? pick_mode<kRanges>(in_mode, ca.bits, upl)
+                    : dm == kDevParams ? pick_mode<kDevParams>(in_mode, ca.bits, upl)
+                                       : pick_mode<kStatic>(in_mode, ca.bits, upl);
+    if (!k) return hipErrorInvalidValue;
+    const int esz = in_mode == RPTQ_IN_FP16_RAW ? 2 : 4;
+    const int ch = upl * esz / 2, och = (upl * ca.bits + 15) / 16;
+    // reduction scratch (64 floats), then (ranges pass) the (lo, hi) of every
+    // 32-code group
+    const size_t extra = 256 + (dm == kRanges ? (size_t)(2 * (ca.K_pad / 32)) * 4 : 0);
+    const size_t lds = (size_t)ch * 16 * block + (size_t)och * 16 * block + 16 + extra;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const int grid = persistent_grid(k, block, lds, M);
+    void* args[] = {(void*)&x, (void*)&M, (void*)&K, (void*)&row_bytes, (void*)&gamma_r,
+                    (void*)&beta_r, (void*)&eps, (void*)&R, (void*)&ca, (void*)&codes, (void*)&dyn_a,
+                    (void*)&dyn_b};
+    return hipLaunchKernel(k, dim3(grid), dim3(block), args, lds, stream);
 }
 
 }  // namespace
@@ -237,26 +397,28 @@ hipError_t launch_ln_reorder_quant(const void* x, int in_mode, int64_t M, int32_
                                    const float* gamma_r, const float* beta_r, float eps,
                                    const int32_t* R, const ClusterArgs& ca, int64_t row_bytes,
                                    uint8_t* codes, hipStream_t stream) {
-    int upl = 0, block = 0;
-    unit_split(ca.K_pad / 8, upl, block, RPTQ_LN_MAX_BLOCK);
-    const void* k = nullptr;
-    if (in_mode == RPTQ_IN_FP16_RAW) {
-        k = ca.bits == 3 ? pick<3, 0>(upl) : ca.bits == 4 ? pick<4, 0>(upl) : pick<8, 0>(upl);
-    } else {
-        k = ca.bits == 3 ? pick<3, 1>(upl) : ca.bits == 4 ? pick<4, 1>(upl) : pick<8, 1>(upl);
-    }
-    if (!k) return hipErrorInvalidValue;
-    const int esz = in_mode == RPTQ_IN_FP16_RAW ? 2 : 4;
-    const int ch = upl * esz / 2, och = (upl * ca.bits + 15) / 16;
-    const size_t lds = (size_t)ch * 16 * block + (size_t)och * 16 * block + 16 + 256;
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    const int grid = persistent_grid(k, block, lds, M);
-    void* args[] = {(void*)&x, (void*)&M, (void*)&K, (void*)&row_bytes, (void*)&gamma_r,
-                    (void*)&beta_r, (void*)&eps, (void*)&R, (void*)&ca, (void*)&codes};
-    return hipLaunchKernel(k, dim3(grid), dim3(block), args, lds, stream);
+    return launch_mode(kStatic, x, in_mode, M, K, gamma_r, beta_r, eps, R, ca, row_bytes, codes, nullptr,
+                       nullptr, stream);
+}
+
+hipError_t launch_ln_reorder_quant_dynamic(const void* x, int in_mode, int64_t M, int32_t K,
+                                           const float* gamma_r, const float* beta_r, float eps,
+                                           const int32_t* R, const ClusterArgs& ca, int64_t row_bytes,
+                                           uint8_t* codes, float* s_out, int32_t* z_out, hipStream_t stream) {
+    // (lo, hi) accumulate in s_out (hi) and z_out (lo, float bits), then
+    // become (s, z) in place; four launches in stream order
+    dynamic_init_kernel<<<dim3(1), dim3(64), 0, stream>>>(s_out, z_out, ca.g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_mode(kRanges, x, in_mode, M, K, gamma_r, beta_r, eps, R, ca, row_bytes, codes, s_out, z_out,
+                    stream);
+    if (e != hipSuccess) return e;
+    if (ca.bits == 3) dynamic_params_kernel<3><<<dim3(1), dim3(64), 0, stream>>>(s_out, z_out, ca.g);
+    else if (ca.bits == 4) dynamic_params_kernel<4><<<dim3(1), dim3(64), 0, stream>>>(s_out, z_out, ca.g);
+    else dynamic_params_kernel<8><<<dim3(1), dim3(64), 0, stream>>>(s_out, z_out, ca.g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_mode(kDevParams, x, in_mode, M, K, gamma_r, beta_r, eps, R, ca, row_bytes, codes, s_out,
+                       z_out, stream);
 }
 
 }  // namespace rptq

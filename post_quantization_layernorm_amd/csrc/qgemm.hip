@@ -185,7 +185,17 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     // cluster count: a scalar load of it would be pending in the loop and
     // turn the waits there into waits for every LDS read)
     const int end_l = lane < ga.g ? ga.step_end[lane] : 0x7fffffff;
-    const float d_l = lane < ga.g ? ga.scale[lane] : 0.0f;
+    float d_l;
+    if (ga.dev_s) {
+        // dynamic ranges: d_c = s_c - s_(c+1) from the device table, formed
+        // like the host forms it for calibrated (s, z)
+        const double sc = lane < ga.g ? (double)ga.dev_s[lane] : 0.0;
+        const double sn = lane + 1 < ga.g ? (double)ga.dev_s[lane + 1] : 0.0;
+        const double d = sc - sn;
+        d_l = (float)(WBITS == 4 ? d * 0.0625 : WBITS == 3 ? d * 0.03125 : d);
+    } else {
+        d_l = lane < ga.g ? ga.scale[lane] : 0.0f;
+    }
     asm volatile("" ::"v"(end_l), "v"(d_l) : "memory");
 
     // ---- staging: piece p = tid + i * NT covers row p / SK, step p % SK of a stage
@@ -409,7 +419,13 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
         const int n = n0 + wn * 64 + j * 32 + col_l;
         if (n >= N) continue;
         double corr = 0.0;
-        for (int cc = 0; cc < ga.g; ++cc) corr += ga.sz[cc] * (double)colsum[(int64_t)cc * N + n];
+        if (ga.dev_s) {
+            for (int cc = 0; cc < ga.g; ++cc)
+                corr += (double)ga.dev_s[cc] * ((double)ga.dev_z[cc] - (double)ga.code_offset) *
+                        (double)colsum[(int64_t)cc * N + n];
+        } else {
+            for (int cc = 0; cc < ga.g; ++cc) corr += ga.sz[cc] * (double)colsum[(int64_t)cc * N + n];
+        }
         const double sw = (double)s_w[n];
         // the next layer's cluster of position n (pad positions: no cluster)
         float inv = 0.0f, zf = 0.0f;

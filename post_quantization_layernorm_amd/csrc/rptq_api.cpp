@@ -195,19 +195,58 @@ int rptq_ln_reorder_quant(const void* x, int32_t in_mode, int64_t M, int32_t K,
                       "rptq_ln_reorder_quant launch");
 }
 
-// Shared by rptq_qgemm and rptq_qgemm_quant: validation of the GEMM proper,
+int rptq_ln_reorder_quant_dynamic(const void* x, int32_t in_mode, int64_t M, int32_t K,
+                                  const float* gamma_r, const float* beta_r, float eps,
+                                  const int32_t* R, const int32_t* bounds, int32_t g, int32_t bits,
+                                  uint8_t* codes, float* s_out, int32_t* z_out, void* stream) {
+    if (in_mode != RPTQ_IN_FP16_RAW && in_mode != RPTQ_IN_FP32_NORMALIZED)
+        return fail(RPTQ_ERR_INVALID_ARG, "in_mode = %d", in_mode);
+    if (M < 1) return fail(RPTQ_ERR_INVALID_ARG, "M = %lld < 1: dynamic ranges need rows", (long long)M);
+    if (K < 1) return fail(RPTQ_ERR_INVALID_ARG, "K = %d < 1", K);
+    if (!valid_bits(bits)) return fail(RPTQ_ERR_INVALID_ARG, "bits = %d not in {3, 4, 8}", bits);
+    int st = check_bounds(bounds, g, K);
+    if (st) return st;
+    if (in_mode == RPTQ_IN_FP16_RAW) {
+        if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(RPTQ_ERR_INVALID_ARG, "eps must be finite and > 0");
+        if (!gamma_r || !beta_r) return fail(RPTQ_ERR_INVALID_ARG, "gamma_r / beta_r is NULL");
+    }
+    if (K % 8) return fail(RPTQ_ERR_UNSUPPORTED, "K = %d is not a multiple of 8", K);
+    if (K > kMaxK) return fail(RPTQ_ERR_UNSUPPORTED, "K = %d exceeds %d", K, kMaxK);
+    if (!x || !codes || !s_out || !z_out) return fail(RPTQ_ERR_INVALID_ARG, "x, codes, s_out or z_out is NULL");
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(s_out) || !aligned16(z_out) ||
+        (in_mode == RPTQ_IN_FP16_RAW && (!aligned16(gamma_r) || !aligned16(beta_r) || (R && !aligned16(R)))))
+        return fail(RPTQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    // the cluster table's own (s, z) are unused: placeholders
+    float s1[kMaxClusters];
+    int32_t z0[kMaxClusters];
+    for (int c = 0; c < g; ++c) { s1[c] = 1.0f; z0[c] = 0; }
+    const ClusterArgs ca = make_cluster_args(bounds, g, s1, z0, bits, true);
+    const int64_t row_bytes = (int64_t)ca.K_pad * bits / 8;
+    return hip_status(launch_ln_reorder_quant_dynamic(x, in_mode, M, K, gamma_r, beta_r, eps,
+                                                      in_mode == RPTQ_IN_FP16_RAW ? R : nullptr, ca, row_bytes,
+                                                      codes, s_out, z_out, (hipStream_t)stream),
+                      "rptq_ln_reorder_quant_dynamic launch");
+}
+
+// Shared by rptq_qgemm, rptq_qgemm_dynamic and rptq_qgemm_quant: validation of the GEMM proper,
 // the per-cluster tables, the launch.
 static int qgemm_common(const uint8_t* codes, int64_t M, int32_t K, int32_t N, const int32_t* bounds,
                         int32_t g, const float* s, const int32_t* z, int32_t a_bits, const uint8_t* w_packed,
                         int32_t w_bits, const float* s_w, const int32_t* colsum, float* Y, int32_t* acc_debug,
-                        const QuantOutArgs& qo, const ClusterArgs& qc, void* stream, const char* what) {
+                        const QuantOutArgs& qo, const ClusterArgs& qc, void* stream, const char* what,
+                        bool dev_params = false) {
     if (M < 0) return fail(RPTQ_ERR_INVALID_ARG, "M = %lld < 0", (long long)M);
     if (K < 1 || N < 1) return fail(RPTQ_ERR_INVALID_ARG, "K = %d, N = %d must be >= 1", K, N);
     if (!valid_bits(a_bits)) return fail(RPTQ_ERR_INVALID_ARG, "a_bits = %d not in {3, 4, 8}", a_bits);
     if (!valid_wbits(w_bits)) return fail(RPTQ_ERR_INVALID_ARG, "w_bits = %d not in {3, 4, 8}", w_bits);
     int st = check_bounds(bounds, g, K);
     if (st) return st;
-    if ((st = check_params(s, z, g))) return st;
+    if (dev_params) {
+        if (!s || !z) return fail(RPTQ_ERR_INVALID_ARG, "s or z is NULL");
+        if (!aligned16(s) || !aligned16(z)) return fail(RPTQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    } else if ((st = check_params(s, z, g))) {
+        return st;
+    }
     if (K > kMaxK) return fail(RPTQ_ERR_UNSUPPORTED, "K = %d exceeds %d", K, kMaxK);
     if (M == 0) return ok();
     if (!codes || !w_packed || !s_w || !colsum || (!Y && !qo.q_codes))
@@ -223,14 +262,20 @@ static int qgemm_common(const uint8_t* codes, int64_t M, int32_t K, int32_t N, c
     for (int c = 0; c < g; ++c) {
         steps += (bounds[c + 1] - bounds[c] + 31) / 32;
         ga.step_end[c] = steps;
-        ga.sz[c] = (double)s[c] * ((double)z[c] - (double)ga.code_offset);
     }
-    // flush weights of the running accumulator: d_c = s_c - s_(c+1), s_(g+1) = 0
-    // (4-bit weights are staged as 16 * w and 3-bit weights as 32 * w, hence
-    // the 1/16 and 1/32)
-    for (int c = 0; c < g; ++c) {
-        const double d = (double)s[c] - (c + 1 < g ? (double)s[c + 1] : 0.0);
-        ga.scale[c] = (float)(w_bits == 4 ? d * 0.0625 : w_bits == 3 ? d * 0.03125 : d);
+    if (dev_params) {
+        // the kernel forms the tables below from the device (s, z)
+        ga.dev_s = s;
+        ga.dev_z = z;
+    } else {
+        for (int c = 0; c < g; ++c) ga.sz[c] = (double)s[c] * ((double)z[c] - (double)ga.code_offset);
+        // flush weights of the running accumulator: d_c = s_c - s_(c+1), s_(g+1) = 0
+        // (4-bit weights are staged as 16 * w and 3-bit weights as 32 * w, hence
+        // the 1/16 and 1/32)
+        for (int c = 0; c < g; ++c) {
+            const double d = (double)s[c] - (c + 1 < g ? (double)s[c + 1] : 0.0);
+            ga.scale[c] = (float)(w_bits == 4 ? d * 0.0625 : w_bits == 3 ? d * 0.03125 : d);
+        }
     }
     ga.nsteps = steps;
     const int64_t a_row_bytes = (int64_t)steps * 32 * a_bits / 8;
@@ -249,6 +294,18 @@ int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N, const int3
     std::memset(&qc, 0, sizeof qc);
     return qgemm_common(codes, M, K, N, bounds, g, s, z, a_bits, w_packed, w_bits, s_w, colsum, Y, acc_debug,
                         qo, qc, stream, "rptq_qgemm launch");
+}
+
+int rptq_qgemm_dynamic(const uint8_t* codes, int64_t M, int32_t K, int32_t N, const int32_t* bounds,
+                       int32_t g, const float* s_dev, const int32_t* z_dev, int32_t a_bits,
+                       const uint8_t* w_packed, int32_t w_bits, const float* s_w, const int32_t* colsum,
+                       float* Y, void* stream) {
+    if (M > 0 && !Y) return fail(RPTQ_ERR_INVALID_ARG, "Y must be non-NULL");
+    QuantOutArgs qo{nullptr, 0, 0};
+    ClusterArgs qc;
+    std::memset(&qc, 0, sizeof qc);
+    return qgemm_common(codes, M, K, N, bounds, g, s_dev, z_dev, a_bits, w_packed, w_bits, s_w, colsum, Y,
+                        nullptr, qo, qc, stream, "rptq_qgemm_dynamic launch", true);
 }
 
 int rptq_qgemm_quant(const uint8_t* codes, int64_t M, int32_t K, int32_t N_pad, const int32_t* bounds,

@@ -56,6 +56,10 @@ struct GemmArgs {
     float scale[kMaxClusters];             // (s_c - s_(c+1)) divided by the weight pre-scale
     double sz[kMaxClusters];               // s_c * (z_c - code offset), for the epilogue
     int32_t code_offset;                   // 128 for 8-bit activations (stored q - 128), else 0
+    // device-resident (s, z) [g] (dynamic ranges): when set, the kernel forms
+    // scale[] and sz[] from them itself and the two tables above are unused
+    const float* dev_s;
+    const int32_t* dev_z;
 };
 
 // Launchers (one per kernel family); each returns the launch status.
@@ -63,6 +67,13 @@ hipError_t launch_ln_reorder_quant(const void* x, int in_mode, int64_t M, int32_
                                    const float* gamma_r, const float* beta_r, float eps,
                                    const int32_t* R, const ClusterArgs& ca, int64_t row_bytes,
                                    uint8_t* codes, hipStream_t stream);
+
+// Dynamic ranges: per-cluster (lo, hi) over the batch, then (s, z) into
+// s_out / z_out (device [g]), then the quantization with them.
+hipError_t launch_ln_reorder_quant_dynamic(const void* x, int in_mode, int64_t M, int32_t K,
+                                           const float* gamma_r, const float* beta_r, float eps,
+                                           const int32_t* R, const ClusterArgs& ca, int64_t row_bytes,
+                                           uint8_t* codes, float* s_out, int32_t* z_out, hipStream_t stream);
 
 hipError_t launch_kv_quant_pack(const uint16_t* kv, int64_t T, int32_t C, const int32_t* R,
                                 const ClusterArgs& ca, uint8_t* packed, hipStream_t stream);

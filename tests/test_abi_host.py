@@ -90,6 +90,50 @@ def test_ln_reorder_quant_m0_is_noop(P):
     assert _ln(P, M=0, mode=1, gamma=None, beta=None, eps=0.0) == 0
 
 
+def _ln_dyn(P, **kw):
+    a = dict(x=FAKE, mode=0, M=4, K=64, gamma=FAKE, beta=FAKE, eps=1e-5, R=None,
+             bounds=np.array([0, 16, 64], np.int32), bits=4, codes=FAKE, s=FAKE, z=FAKE)
+    a.update(kw)
+    return P.lib().rptq_ln_reorder_quant_dynamic(a["x"], a["mode"], a["M"], a["K"], a["gamma"], a["beta"],
+                                                 a["eps"], a["R"], _vp(a["bounds"]), a["bounds"].size - 1,
+                                                 a["bits"], a["codes"], a["s"], a["z"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=5), -1), (dict(mode=7), -1), (dict(M=0), -1), (dict(M=-1), -1), (dict(K=0), -1),
+    (dict(bounds=np.array([0, 16, 60], np.int32)), -1), (dict(bounds=np.array([0, 16, 16, 64], np.int32)), -1),
+    (dict(eps=0.0), -1), (dict(gamma=None), -1), (dict(x=None), -1), (dict(codes=None), -1),
+    (dict(s=None), -1), (dict(z=None), -1),
+    (dict(K=60, bounds=np.array([0, 16, 60], np.int32)), -2),
+    (dict(x=MISALIGNED), -3), (dict(s=MISALIGNED), -3), (dict(z=MISALIGNED), -3),
+])
+def test_ln_reorder_quant_dynamic_rejects(P, kw, status):
+    assert _ln_dyn(P, **kw) == status
+    assert P.lib().rptq_last_error().decode()
+
+
+def _gemm_dyn(P, **kw):
+    a = dict(codes=FAKE, M=8, K=64, N=32, bounds=np.array([0, 16, 64], np.int32), s=FAKE, z=FAKE, a_bits=4,
+             w=FAKE, w_bits=4, s_w=FAKE, colsum=FAKE, Y=FAKE)
+    a.update(kw)
+    return P.lib().rptq_qgemm_dynamic(a["codes"], a["M"], a["K"], a["N"], _vp(a["bounds"]),
+                                      a["bounds"].size - 1, a["s"], a["z"], a["a_bits"], a["w"], a["w_bits"],
+                                      a["s_w"], a["colsum"], a["Y"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a_bits=2), -1), (dict(w_bits=2), -1), (dict(N=0), -1), (dict(K=63), -1), (dict(s=None), -1),
+    (dict(z=None), -1), (dict(Y=None), -1), (dict(colsum=None), -1),
+    (dict(s=MISALIGNED), -3), (dict(Y=MISALIGNED), -3),
+])
+def test_qgemm_dynamic_rejects(P, kw, status):
+    assert _gemm_dyn(P, **kw) == status
+
+
+def test_qgemm_dynamic_m0_is_noop(P):
+    assert _gemm_dyn(P, M=0, codes=None, Y=None) == 0
+
+
 def _gemm(P, **kw):
     a = dict(codes=FAKE, M=8, K=64, N=32, bounds=np.array([0, 16, 64], np.int32),
              s=np.array([0.1, 0.2], np.float32), z=np.array([3, -2], np.int32), a_bits=4, w=FAKE, w_bits=4,

@@ -100,6 +100,41 @@ def test_fc1_fullsize_gemm_sampled(P, fc1, ab, wb):
     assert np.array_equal(acc.cpu().numpy(), acc64)
 
 
+def test_fc1_fullsize_dynamic_sampled(P, fc1):
+    """Dynamic ranges over the whole 16384-token batch: (s, z) against the
+    oracle's (its ranges see every row), sampled rows' codes against the
+    oracle's, and the device-scale GEMM equal to the host-scale one."""
+    M, K, N, g = fc1["M"], fc1["K"], fc1["N"], fc1["g"]
+    R, bounds, _, _ = fc1["params"][4]
+    Wq, s_w = fc1["wq"][4]
+    _say("dynamic ln + gemm")
+    y = orc.layernorm(fc1["x"], fc1["gamma"], fc1["beta"], 1e-5, R)
+    s_o, z_o = orc.dynamic_cluster_params(y, bounds, 4)
+    want = orc.pack_seg32(orc.quantize(y[ROWS], bounds, s_o, z_o, 4), bounds, 4)
+    del y
+    xd = dev(fc1["x"].view(np.int16)).view(torch.float16)
+    codes, sd, zd = P.rptq_ln_reorder_quant_dynamic(xd, dev(R), dev(fc1["gamma"][R]), dev(fc1["beta"][R]),
+                                                    bounds, 4)
+    sh, zh = sd.cpu().numpy(), zd.cpu().numpy()
+    assert np.abs(sh.astype(np.float64) / s_o - 1.0).max() <= 1e-5
+    assert np.abs(zh.astype(np.int64) - z_o).max() <= 1
+    qg, pad = orc.unpack_seg32(codes[torch.from_numpy(ROWS).cuda()].cpu().numpy(), K, bounds, 4, return_pad=True)
+    qw = orc.unpack_seg32(want, K, bounds, 4)
+    d = np.abs(qg.astype(np.int32) - qw.astype(np.int32))
+    assert not pad.any()
+    assert d.max() <= 1 and (d > 0).mean() <= 1e-3, (d.max(), (d > 0).mean())
+    del xd
+    wp, cs = P.rptq_pack_weights(Wq, R, bounds, 4)
+    wp, cs, sw = dev(wp), dev(cs), dev(s_w)
+    Y = P.rptq_qgemm_dynamic(codes, M, K, N, bounds, sd, zd, 4, wp, 4, sw, cs)
+    Ys = P.rptq_qgemm(codes, M, K, N, bounds, sh, zh, 4, wp, 4, sw, cs)
+    assert torch.equal(Y, Ys)
+    del Ys
+    q = orc.unpack_seg32(codes[torch.from_numpy(ROWS).cuda()].cpu().numpy(), K, bounds, 4)
+    Y_o = orc.qgemm(q, Wq, R, bounds, sh, zh, s_w)
+    assert rel_l2(Y[torch.from_numpy(ROWS).cuda()].cpu().numpy(), Y_o) <= 1e-3
+
+
 def test_kv_fullsize_sampled(P):
     kw = synthetic.KV_WORKLOADS["opt66b_kv_a3"]
     T, C, g, bits = kw.T, kw.C, kw.g, kw.bits

@@ -155,6 +155,84 @@ def test_ln_m0_noop(P):
     assert out.shape[0] == 0
 
 
+# ----------------------------------------------------------------------------- dynamic ranges
+DYN_SHAPES = [  # (M, K, g, outlier_frac, range_ratio)
+    (128, 768, 4, 0.01, None),
+    (41, 9216, 32, 0.01, None),
+    (6, 16384, 64, 0.01, None),
+    (1, 2048, 8, 0.0, None),            # one row
+    (3001, 1024, 8, 0.01, None),        # many rows per workgroup, odd row count
+]
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+@pytest.mark.parametrize("shape", DYN_SHAPES, ids=lambda s: f"M{s[0]}K{s[1]}g{s[2]}")
+def test_ln_dynamic_quant_only_bit_exact(P, bits, shape):
+    """Dynamic ranges in quant-only mode: (s, z) and the codes equal the
+    oracle's bit for bit; a second call on other rows with the same (s, z)
+    buffers starts its ranges afresh."""
+    M, K, g, frac, rr = shape
+    _say("ln dynamic quant-only", bits, shape)
+    c = layer_case(M, K, 8, g, bits, seed=3 * K + bits, outlier_frac=frac, range_ratio=rr, with_weights=False)
+    y = orc.layernorm(c.x, c.gamma, c.beta, 1e-5, c.R)
+    y[0, :4] = [0.0, -0.0, 1e-3, -1e-3]
+    sd = torch.empty(g, dtype=torch.float32, device="cuda")
+    zd = torch.empty(g, dtype=torch.int32, device="cuda")
+    for yy in (y * np.float32(3.0), y):
+        want, s_o, z_o = orc.quantize_dynamic(yy, c.bounds, bits)
+        got, sd, zd = P.rptq_ln_reorder_quant_dynamic(dev(yy), None, None, None, c.bounds, bits,
+                                                      in_mode=P.RPTQ_IN_FP32_NORMALIZED, s_out=sd, z_out=zd)
+        torch.cuda.synchronize()
+        assert np.array_equal(sd.cpu().numpy(), s_o)
+        assert np.array_equal(zd.cpu().numpy(), z_o)
+        assert np.array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+@pytest.mark.parametrize("shape", DYN_SHAPES, ids=lambda s: f"M{s[0]}K{s[1]}g{s[2]}")
+def test_ln_dynamic_fused_within_tolerance(P, bits, shape):
+    """Fused LayerNorm with dynamic ranges: s within 1e-5 relative of the
+    oracle's (the kernel's fp32 LayerNorm moves the extremes by a few ulps),
+    z within 1, codes as for the calibrated path (at most 0.1% differ, by 1)."""
+    M, K, g, frac, rr = shape
+    _say("ln dynamic fused", bits, shape)
+    c = layer_case(M, K, 8, g, bits, seed=3 * K + bits, outlier_frac=frac, range_ratio=rr, with_weights=False)
+    want, s_o, z_o = orc.ln_reorder_quant_dynamic(c.x, c.gamma, c.beta, 1e-5, c.R, c.bounds, bits)
+    gr, br = c.gamma[c.R], c.beta[c.R]
+    got, sd, zd = P.rptq_ln_reorder_quant_dynamic(dev(c.x.view(np.int16)).view(torch.float16), dev(c.R),
+                                                  dev(gr), dev(br), c.bounds, bits)
+    sg, zg = sd.cpu().numpy(), zd.cpu().numpy()
+    assert np.abs(sg.astype(np.float64) / s_o - 1.0).max() <= 1e-5
+    assert np.abs(zg.astype(np.int64) - z_o).max() <= 1
+    qg, pad = orc.unpack_seg32(got.cpu().numpy(), K, c.bounds, bits, return_pad=True)
+    qw = orc.unpack_seg32(want, K, c.bounds, bits)
+    assert not pad.any()
+    d = np.abs(qg.astype(np.int32) - qw.astype(np.int32))
+    assert d.max() <= 1 and (d > 0).mean() <= 1e-3, (d.max(), (d > 0).mean())
+
+
+@pytest.mark.parametrize("ab,wb", [(4, 4), (3, 3), (8, 8), (8, 4), (3, 4)])
+def test_qgemm_dynamic(P, ab, wb):
+    """The GEMM reading (s, z) from device memory: Y equals rptq_qgemm's with
+    the same (s, z) passed from the host, bit for bit, and the oracle's GEMM
+    of the kernel's codes within 1e-3."""
+    M, K, N, g = 150, 2048, 520, 8
+    _say("gemm dynamic", ab, wb)
+    c = layer_case(M, K, N, g, ab, wb, seed=900 + ab + wb)
+    gr, br = c.gamma[c.R], c.beta[c.R]
+    codes, sd, zd = P.rptq_ln_reorder_quant_dynamic(dev(c.x.view(np.int16)).view(torch.float16), dev(c.R),
+                                                    dev(gr), dev(br), c.bounds, ab)
+    wp, cs, sw = _gemm_inputs(P, c)
+    Y = P.rptq_qgemm_dynamic(codes, M, K, N, c.bounds, sd, zd, ab, wp, wb, sw, cs)
+    sh, zh = sd.cpu().numpy(), zd.cpu().numpy()
+    Y_s = P.rptq_qgemm(codes, M, K, N, c.bounds, sh, zh, ab, wp, wb, sw, cs)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y_s)
+    q = orc.unpack_seg32(codes.cpu().numpy(), K, c.bounds, ab)
+    Y_o = orc.qgemm(q, c.Wq, c.R, c.bounds, sh, zh, c.s_w)
+    assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
+
+
 # ----------------------------------------------------------------------------- GEMM
 def _gemm_inputs(P, c):
     wp, cs = P.rptq_pack_weights(c.Wq, c.R, c.bounds, c.w_bits)
