@@ -196,11 +196,15 @@ int rptq_qgemm_quant(const uint8_t* codes, int64_t M, int32_t K, int32_t N_pad,
  * with y as rptq_ln_reorder_quant defines it for in_mode, and then the codes
  * are that function's codes with these (s, z) (no value is clipped beyond
  * rounding, since every value lies inside its cluster's range).
- * Four launches in stream order: (lo, hi) init, a ranges pass over x
- * (float atomics per cluster), the (s, z) step, the quantizing pass; x is
- * read twice.
- * s_out    device fp32 [g]: receives s (used as scratch during the call).
- * z_out    device int32 [g]: receives z (likewise).
+ * Three launches in stream order: a ranges pass over x (each workgroup
+ * writes its own per-cluster (lo, hi) to the workspace), the (s, z) step
+ * (one workgroup per cluster), the quantizing pass; x is read twice.
+ * s_out    device fp32 [g]: receives s.
+ * z_out    device int32 [g]: receives z.
+ * workspace device, caller-owned, 16-byte aligned, at least
+ *          rptq_ln_dynamic_workspace_bytes(g) bytes; its contents on entry
+ *          do not matter and are undefined on return.  Calls that share a
+ *          workspace must be ordered on one stream.
  * M >= 1 (ranges of no rows are undefined: RPTQ_ERR_INVALID_ARG).  Other
  * arguments, limits and errors as rptq_ln_reorder_quant, without s and z.
  * Magnitudes below about 2^-100 are outside the supported range (1/s must
@@ -209,7 +213,12 @@ int rptq_qgemm_quant(const uint8_t* codes, int64_t M, int32_t K, int32_t N_pad,
 int rptq_ln_reorder_quant_dynamic(const void* x, int32_t in_mode, int64_t M, int32_t K,
                                   const float* gamma_r, const float* beta_r, float eps,
                                   const int32_t* R, const int32_t* bounds, int32_t g, int32_t bits,
-                                  uint8_t* codes, float* s_out, int32_t* z_out, void* stream);
+                                  uint8_t* codes, float* s_out, int32_t* z_out, void* workspace,
+                                  int64_t workspace_bytes, void* stream);
+
+/* Workspace of rptq_ln_reorder_quant_dynamic for g clusters (1024 * 2 * g
+ * floats); -1 if g is outside [1, RPTQ_MAX_CLUSTERS]. */
+int64_t rptq_ln_dynamic_workspace_bytes(int32_t g);
 
 /*
  * rptq_qgemm with the activation clusters' (s, z) in DEVICE memory (s_dev

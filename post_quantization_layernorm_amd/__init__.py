@@ -35,7 +35,8 @@ RPTQ_MAX_CLUSTERS = 64
 RPTQ_MAX_K = 16384
 
 EXPORTED = [
-    "rptq_ln_reorder_quant", "rptq_ln_reorder_quant_dynamic", "rptq_qgemm", "rptq_qgemm_dynamic",
+    "rptq_ln_reorder_quant", "rptq_ln_reorder_quant_dynamic", "rptq_ln_dynamic_workspace_bytes",
+    "rptq_qgemm", "rptq_qgemm_dynamic",
     "rptq_qgemm_quant", "rptq_kv_quant_pack", "rptq_kv_dequant",
     "rptq_kv_attention", "rptq_kv_attention_workspace_bytes",
     "rptq_calib_minmax", "rptq_kmeans_reorder", "rptq_cluster_params", "rptq_quantize_weights",
@@ -73,7 +74,8 @@ def lib() -> ctypes.CDLL:
             "rptq_ln_reorder_quant": (_I32, [_P, _I32, _I64, _I32, _P, _P, ctypes.c_float, _P, _P, _I32,
                                              _P, _P, _I32, _P, _P]),
             "rptq_ln_reorder_quant_dynamic": (_I32, [_P, _I32, _I64, _I32, _P, _P, ctypes.c_float, _P, _P,
-                                                     _I32, _I32, _P, _P, _P, _P]),
+                                                     _I32, _I32, _P, _P, _P, _P, _I64, _P]),
+            "rptq_ln_dynamic_workspace_bytes": (_I64, [_I32]),
             "rptq_qgemm": (_I32, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
             "rptq_qgemm_dynamic": (_I32, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _P,
                                           _P]),
@@ -181,10 +183,17 @@ def rptq_ln_reorder_quant(x, R, gamma_r, beta_r, bounds, s, z, bits, eps=1e-5,
     return out
 
 
+def rptq_ln_dynamic_workspace_bytes(g: int) -> int:
+    return int(lib().rptq_ln_dynamic_workspace_bytes(g))
+
+
 def rptq_ln_reorder_quant_dynamic(x, R, gamma_r, beta_r, bounds, bits, eps=1e-5,
-                                  in_mode=RPTQ_IN_FP16_RAW, out=None, s_out=None, z_out=None, stream=None):
+                                  in_mode=RPTQ_IN_FP16_RAW, out=None, s_out=None, z_out=None, workspace=None,
+                                  stream=None):
     """Dynamic ranges: the clusters' (s, z) come from this batch.  Returns
-    (codes cuda uint8 [M][row_bytes], s cuda fp32 [g], z cuda int32 [g])."""
+    (codes cuda uint8 [M][row_bytes], s cuda fp32 [g], z cuda int32 [g]).
+    workspace: cuda uint8 of at least rptq_ln_dynamic_workspace_bytes(g)
+    bytes (allocated here when None)."""
     M, K = x.shape
     b = _h(bounds, np.int32); g = b.size - 1
     rb = rptq_codes_row_bytes(b, bits)
@@ -196,9 +205,11 @@ def rptq_ln_reorder_quant_dynamic(x, R, gamma_r, beta_r, bounds, bits, eps=1e-5,
         s_out = torch.empty(max(g, 1), dtype=torch.float32, device=x.device)
     if z_out is None:
         z_out = torch.empty(max(g, 1), dtype=torch.int32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(rptq_ln_dynamic_workspace_bytes(g), 16), dtype=torch.uint8, device=x.device)
     st = lib().rptq_ln_reorder_quant_dynamic(_dp(x), in_mode, M, K, _dp(gamma_r), _dp(beta_r), eps, _dp(R),
-                                             _hp(b), g, bits, _dp(out), _dp(s_out), _dp(z_out),
-                                             _stream(stream))
+                                             _hp(b), g, bits, _dp(out), _dp(s_out), _dp(z_out), _dp(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "rptq_ln_reorder_quant_dynamic")
     return out, s_out, z_out
 

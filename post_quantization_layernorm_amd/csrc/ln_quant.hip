@@ -45,18 +45,6 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
 // of the batch's values over the cluster's channels, by the same rules as the
 // calibrated parameters (s = (hi - lo)/qmax in fp32, floored at
 // max(|lo|, |hi|) 2^-21, 1 for an all-zero cluster; z = rne(-lo/s)).
-// float max / min by integer atomics: for IEEE floats (no -0), signed-integer
-// order matches float order on non-negative values and reversed
-// unsigned-integer order matches it on negative ones
-__device__ __forceinline__ void atomic_fmax(float* addr, float v) {
-    if (v >= 0.0f) atomicMax(reinterpret_cast<int*>(addr), __builtin_bit_cast(int, v));
-    else atomicMin(reinterpret_cast<unsigned int*>(addr), __builtin_bit_cast(unsigned int, v));
-}
-__device__ __forceinline__ void atomic_fmin(float* addr, float v) {
-    if (v >= 0.0f) atomicMin(reinterpret_cast<int*>(addr), __builtin_bit_cast(int, v));
-    else atomicMax(reinterpret_cast<unsigned int*>(addr), __builtin_bit_cast(unsigned int, v));
-}
-
 __device__ __forceinline__ void dynamic_params(float lo, float hi, int qmax, float& s, int32_t& z) {
     const double dlo = lo, dhi = hi;
     float sc = (float)((dhi - dlo) / (double)qmax);
@@ -68,9 +56,9 @@ __device__ __forceinline__ void dynamic_params(float lo, float hi, int qmax, flo
 }
 
 // DM (dynamic mode): kStatic quantizes with the (s, z) of the cluster table;
-// kRanges only merges every cluster's min / max over the rows into
-// dyn_lo / dyn_hi (float atomics; no codes written); kDevParams quantizes
-// with the (s, z) found in dyn_s / dyn_z (device memory).
+// kRanges writes no codes, only this workgroup's min and max of every
+// cluster over its rows (dyn_a[blockIdx][0..g) = lo, [g..2g) = hi);
+// kDevParams quantizes with the (s, z) in dyn_a / dyn_b (device memory).
 enum { kStatic = 0, kRanges = 1, kDevParams = 2 };
 
 template <int BITS, int MODE, int UPL, int DM>
@@ -135,8 +123,10 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = p0 + e * UnitGeom<BITS>::stride - ca.off[c];
-                if (i < n_c) {
-                    const int j = ca.bounds[c] + i;
+                // ranges pass: a padding position repeats the cluster's first
+                // channel, which leaves the cluster's min and max unchanged
+                if (i < n_c || DM == kRanges) {
+                    const int j = ca.bounds[c] + (i < n_c ? i : 0);
                     if constexpr (LN) {
                         src[u][e] = (R ? R[j] : j) * 2;
                         gam[u][e] = gamma_r[j];
@@ -238,17 +228,16 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
             }
         };
         if constexpr (DM == kRanges) {
-            // running (lo, hi) of every unit over the rows, padding
-            // positions (beta kPad) left out; rows past M add nothing
+            // running (lo, hi) of every unit over the rows (padding
+            // positions repeat a real channel); rows past M add nothing
             if (row < M) {
 #pragma unroll
                 for (int u = 0; u < UPL; ++u)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float y = y_of(u, e);
-                        const bool pad = bet[u][e] == kPad;
-                        ulo[u] = __builtin_fminf(ulo[u], pad ? __builtin_inff() : y);
-                        uhi[u] = __builtin_fmaxf(uhi[u], pad ? -__builtin_inff() : y);
+                        ulo[u] = __builtin_fminf(ulo[u], y);
+                        uhi[u] = __builtin_fmaxf(uhi[u], y);
                     }
             }
             __syncthreads();          // every lane is done with the row and the sums
@@ -284,8 +273,8 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
 
     if constexpr (DM == kRanges) {
         // units -> 32-code groups (4 consecutive units in 4 consecutive
-        // lanes) -> clusters (one wave per cluster at a time) -> device
-        // (lo, hi) by float atomics
+        // lanes) -> clusters (one wave per cluster at a time) -> this
+        // workgroup's (lo, hi) per cluster
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
             float lo = ulo[u], hi = uhi[u];
@@ -311,34 +300,43 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
                 lo = __builtin_fminf(lo, __shfl_xor(lo, o, 64));
                 hi = __builtin_fmaxf(hi, __shfl_xor(hi, o, 64));
             }
-            // a workgroup without rows keeps (+inf, -inf): nothing to merge
-            if (lane == 0 && lo <= hi) {
-                atomic_fmin(reinterpret_cast<float*>(dyn_b) + c, lo + 0.0f);
-                atomic_fmax(dyn_a + c, hi + 0.0f);
+            // (a workgroup without rows leaves (+inf, -inf))
+            if (lane == 0) {
+                dyn_a[(int64_t)blockIdx.x * 2 * ca.g + c] = lo;
+                dyn_a[(int64_t)blockIdx.x * 2 * ca.g + ca.g + c] = hi;
             }
         }
     }
 }
 
-// Cluster (s, z) from the merged (lo, hi), in place: dyn_a[c] holds hi and
-// becomes s, dyn_b[c] holds lo (as float bits) and becomes z.
+// Cluster c = blockIdx.x: (lo, hi) over the ranges pass's nparts workgroup
+// partials, then (s, z).
 template <int BITS>
-__global__ void dynamic_params_kernel(float* __restrict__ dyn_a, int32_t* __restrict__ dyn_b, int32_t g) {
-    const int c = threadIdx.x;
-    if (c >= g) return;
-    const float hi = dyn_a[c], lo = __builtin_bit_cast(float, dyn_b[c]);
-    float sc;
-    int32_t zc;
-    dynamic_params(lo, hi, (1 << BITS) - 1, sc, zc);
-    dyn_a[c] = sc;
-    dyn_b[c] = zc;
-}
-
-__global__ void dynamic_init_kernel(float* __restrict__ dyn_a, int32_t* __restrict__ dyn_b, int32_t g) {
-    const int c = threadIdx.x;
-    if (c < g) {
-        dyn_a[c] = -__builtin_inff();
-        dyn_b[c] = __builtin_bit_cast(int32_t, __builtin_inff());
+__global__ __launch_bounds__(256) void dynamic_params_kernel(const float* __restrict__ part, int32_t nparts,
+                                                             int32_t g, float* __restrict__ s_out,
+                                                             int32_t* __restrict__ z_out) {
+    __shared__ float red[8];
+    const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    float lo = __builtin_inff(), hi = -__builtin_inff();
+    for (int w = tid; w < nparts; w += 256) {
+        lo = __builtin_fminf(lo, part[(int64_t)w * 2 * g + c]);
+        hi = __builtin_fmaxf(hi, part[(int64_t)w * 2 * g + g + c]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        lo = __builtin_fminf(lo, __shfl_xor(lo, o, 64));
+        hi = __builtin_fmaxf(hi, __shfl_xor(hi, o, 64));
+    }
+    if (lane == 0) { red[wv] = lo; red[4 + wv] = hi; }
+    __syncthreads();
+    if (tid == 0) {
+        lo = __builtin_fminf(__builtin_fminf(red[0], red[1]), __builtin_fminf(red[2], red[3]));
+        hi = __builtin_fmaxf(__builtin_fmaxf(red[4], red[5]), __builtin_fmaxf(red[6], red[7]));
+        float sc;
+        int32_t zc;
+        dynamic_params(lo + 0.0f, hi + 0.0f, (1 << BITS) - 1, sc, zc);
+        s_out[c] = sc;
+        z_out[c] = zc;
     }
 }
 
@@ -365,26 +363,37 @@ const void* pick_mode(int in_mode, int bits, int upl) {
 
 namespace {
 
-hipError_t launch_mode(int dm, const void* x, int in_mode, int64_t M, int32_t K, const float* gamma_r,
-                       const float* beta_r, float eps, const int32_t* R, const ClusterArgs& ca,
-                       int64_t row_bytes, uint8_t* codes, float* dyn_a, int32_t* dyn_b, hipStream_t stream) {
-    int upl = 0, block = 0;
+int launch_shape(int dm, int in_mode, const ClusterArgs& ca, int& upl, int& block, const void*& k,
+                 size_t& lds) {
     unit_split(ca.K_pad / 8, upl, block, RPTQ_LN_MAX_BLOCK);
-    const void* k = dm == kRanges ? pick_mode<kRanges>(in_mode, ca.bits, upl)
-                    : dm == kDevParams ? pick_mode<kDevParams>(in_mode, ca.bits, upl)
-                                       : pick_mode<kStatic>(in_mode, ca.bits, upl);
-    if (!k) return hipErrorInvalidValue;
+    k = dm == kRanges ? pick_mode<kRanges>(in_mode, ca.bits, upl)
+        : dm == kDevParams ? pick_mode<kDevParams>(in_mode, ca.bits, upl)
+                           : pick_mode<kStatic>(in_mode, ca.bits, upl);
+    if (!k) return -1;
     const int esz = in_mode == RPTQ_IN_FP16_RAW ? 2 : 4;
     const int ch = upl * esz / 2, och = (upl * ca.bits + 15) / 16;
     // reduction scratch (64 floats), then (ranges pass) the (lo, hi) of every
     // 32-code group
     const size_t extra = 256 + (dm == kRanges ? (size_t)(2 * (ca.K_pad / 32)) * 4 : 0);
-    const size_t lds = (size_t)ch * 16 * block + (size_t)och * 16 * block + 16 + extra;
+    lds = (size_t)ch * 16 * block + (size_t)och * 16 * block + 16 + extra;
+    return 0;
+}
+
+hipError_t launch_mode(int dm, const void* x, int in_mode, int64_t M, int32_t K, const float* gamma_r,
+                       const float* beta_r, float eps, const int32_t* R, const ClusterArgs& ca,
+                       int64_t row_bytes, uint8_t* codes, float* dyn_a, int32_t* dyn_b, int max_grid,
+                       hipStream_t stream, int* grid_out = nullptr) {
+    int upl = 0, block = 0;
+    const void* k = nullptr;
+    size_t lds = 0;
+    if (launch_shape(dm, in_mode, ca, upl, block, k, lds)) return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    const int grid = persistent_grid(k, block, lds, M);
+    int grid = persistent_grid(k, block, lds, M);
+    if (max_grid > 0 && grid > max_grid) grid = max_grid;
+    if (grid_out) *grid_out = grid;
     void* args[] = {(void*)&x, (void*)&M, (void*)&K, (void*)&row_bytes, (void*)&gamma_r,
                     (void*)&beta_r, (void*)&eps, (void*)&R, (void*)&ca, (void*)&codes, (void*)&dyn_a,
                     (void*)&dyn_b};
@@ -398,27 +407,30 @@ hipError_t launch_ln_reorder_quant(const void* x, int in_mode, int64_t M, int32_
                                    const int32_t* R, const ClusterArgs& ca, int64_t row_bytes,
                                    uint8_t* codes, hipStream_t stream) {
     return launch_mode(kStatic, x, in_mode, M, K, gamma_r, beta_r, eps, R, ca, row_bytes, codes, nullptr,
-                       nullptr, stream);
+                       nullptr, 0, stream);
 }
 
 hipError_t launch_ln_reorder_quant_dynamic(const void* x, int in_mode, int64_t M, int32_t K,
                                            const float* gamma_r, const float* beta_r, float eps,
                                            const int32_t* R, const ClusterArgs& ca, int64_t row_bytes,
-                                           uint8_t* codes, float* s_out, int32_t* z_out, hipStream_t stream) {
-    // (lo, hi) accumulate in s_out (hi) and z_out (lo, float bits), then
-    // become (s, z) in place; four launches in stream order
-    dynamic_init_kernel<<<dim3(1), dim3(64), 0, stream>>>(s_out, z_out, ca.g);
-    hipError_t e = hipGetLastError();
+                                           uint8_t* codes, float* s_out, int32_t* z_out, float* partials,
+                                           hipStream_t stream) {
+    // three launches in stream order: per-workgroup (lo, hi) partials, the
+    // clusters' (s, z), the quantizing pass
+    int nparts = 0;
+    hipError_t e = launch_mode(kRanges, x, in_mode, M, K, gamma_r, beta_r, eps, R, ca, row_bytes, codes, partials,
+                               nullptr, kLnRangesMaxGrid, stream, &nparts);
     if (e != hipSuccess) return e;
-    e = launch_mode(kRanges, x, in_mode, M, K, gamma_r, beta_r, eps, R, ca, row_bytes, codes, s_out, z_out,
-                    stream);
-    if (e != hipSuccess) return e;
-    if (ca.bits == 3) dynamic_params_kernel<3><<<dim3(1), dim3(64), 0, stream>>>(s_out, z_out, ca.g);
-    else if (ca.bits == 4) dynamic_params_kernel<4><<<dim3(1), dim3(64), 0, stream>>>(s_out, z_out, ca.g);
-    else dynamic_params_kernel<8><<<dim3(1), dim3(64), 0, stream>>>(s_out, z_out, ca.g);
+    const int32_t g = ca.g;
+    if (ca.bits == 3)
+        dynamic_params_kernel<3><<<dim3(g), dim3(256), 0, stream>>>(partials, nparts, g, s_out, z_out);
+    else if (ca.bits == 4)
+        dynamic_params_kernel<4><<<dim3(g), dim3(256), 0, stream>>>(partials, nparts, g, s_out, z_out);
+    else
+        dynamic_params_kernel<8><<<dim3(g), dim3(256), 0, stream>>>(partials, nparts, g, s_out, z_out);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_mode(kDevParams, x, in_mode, M, K, gamma_r, beta_r, eps, R, ca, row_bytes, codes, s_out,
-                       z_out, stream);
+                       z_out, 0, stream);
 }
 
 }  // namespace rptq

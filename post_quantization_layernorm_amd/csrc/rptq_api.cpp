@@ -198,7 +198,8 @@ int rptq_ln_reorder_quant(const void* x, int32_t in_mode, int64_t M, int32_t K,
 int rptq_ln_reorder_quant_dynamic(const void* x, int32_t in_mode, int64_t M, int32_t K,
                                   const float* gamma_r, const float* beta_r, float eps,
                                   const int32_t* R, const int32_t* bounds, int32_t g, int32_t bits,
-                                  uint8_t* codes, float* s_out, int32_t* z_out, void* stream) {
+                                  uint8_t* codes, float* s_out, int32_t* z_out, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
     if (in_mode != RPTQ_IN_FP16_RAW && in_mode != RPTQ_IN_FP32_NORMALIZED)
         return fail(RPTQ_ERR_INVALID_ARG, "in_mode = %d", in_mode);
     if (M < 1) return fail(RPTQ_ERR_INVALID_ARG, "M = %lld < 1: dynamic ranges need rows", (long long)M);
@@ -212,8 +213,12 @@ int rptq_ln_reorder_quant_dynamic(const void* x, int32_t in_mode, int64_t M, int
     }
     if (K % 8) return fail(RPTQ_ERR_UNSUPPORTED, "K = %d is not a multiple of 8", K);
     if (K > kMaxK) return fail(RPTQ_ERR_UNSUPPORTED, "K = %d exceeds %d", K, kMaxK);
-    if (!x || !codes || !s_out || !z_out) return fail(RPTQ_ERR_INVALID_ARG, "x, codes, s_out or z_out is NULL");
-    if (!aligned16(x) || !aligned16(codes) || !aligned16(s_out) || !aligned16(z_out) ||
+    if (!x || !codes || !s_out || !z_out || !workspace)
+        return fail(RPTQ_ERR_INVALID_ARG, "x, codes, s_out, z_out or workspace is NULL");
+    if (workspace_bytes < rptq_ln_dynamic_workspace_bytes(g))
+        return fail(RPTQ_ERR_INVALID_ARG, "workspace_bytes = %lld < %lld", (long long)workspace_bytes,
+                    (long long)rptq_ln_dynamic_workspace_bytes(g));
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(s_out) || !aligned16(z_out) || !aligned16(workspace) ||
         (in_mode == RPTQ_IN_FP16_RAW && (!aligned16(gamma_r) || !aligned16(beta_r) || (R && !aligned16(R)))))
         return fail(RPTQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
     // the cluster table's own (s, z) are unused: placeholders
@@ -224,8 +229,14 @@ int rptq_ln_reorder_quant_dynamic(const void* x, int32_t in_mode, int64_t M, int
     const int64_t row_bytes = (int64_t)ca.K_pad * bits / 8;
     return hip_status(launch_ln_reorder_quant_dynamic(x, in_mode, M, K, gamma_r, beta_r, eps,
                                                       in_mode == RPTQ_IN_FP16_RAW ? R : nullptr, ca, row_bytes,
-                                                      codes, s_out, z_out, (hipStream_t)stream),
+                                                      codes, s_out, z_out, static_cast<float*>(workspace),
+                                                      (hipStream_t)stream),
                       "rptq_ln_reorder_quant_dynamic launch");
+}
+
+int64_t rptq_ln_dynamic_workspace_bytes(int32_t g) {
+    if (g < 1 || g > kMaxClusters) return -1;
+    return (int64_t)kLnRangesMaxGrid * 2 * g * (int64_t)sizeof(float);
 }
 
 // Shared by rptq_qgemm, rptq_qgemm_dynamic and rptq_qgemm_quant: validation of the GEMM proper,

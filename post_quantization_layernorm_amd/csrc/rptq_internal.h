@@ -68,12 +68,15 @@ hipError_t launch_ln_reorder_quant(const void* x, int in_mode, int64_t M, int32_
                                    const int32_t* R, const ClusterArgs& ca, int64_t row_bytes,
                                    uint8_t* codes, hipStream_t stream);
 
-// Dynamic ranges: per-cluster (lo, hi) over the batch, then (s, z) into
-// s_out / z_out (device [g]), then the quantization with them.
+// Dynamic ranges: per-workgroup (lo, hi) partials of every cluster (at most
+// kLnRangesMaxGrid workgroups, 2 g floats each, in `partials`), then (s, z)
+// into s_out / z_out (device [g]), then the quantization with them.
+constexpr int kLnRangesMaxGrid = 1024;
 hipError_t launch_ln_reorder_quant_dynamic(const void* x, int in_mode, int64_t M, int32_t K,
                                            const float* gamma_r, const float* beta_r, float eps,
                                            const int32_t* R, const ClusterArgs& ca, int64_t row_bytes,
-                                           uint8_t* codes, float* s_out, int32_t* z_out, hipStream_t stream);
+                                           uint8_t* codes, float* s_out, int32_t* z_out, float* partials,
+                                           hipStream_t stream);
 
 hipError_t launch_kv_quant_pack(const uint16_t* kv, int64_t T, int32_t C, const int32_t* R,
                                 const ClusterArgs& ca, uint8_t* packed, hipStream_t stream);

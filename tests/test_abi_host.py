@@ -92,11 +92,13 @@ def test_ln_reorder_quant_m0_is_noop(P):
 
 def _ln_dyn(P, **kw):
     a = dict(x=FAKE, mode=0, M=4, K=64, gamma=FAKE, beta=FAKE, eps=1e-5, R=None,
-             bounds=np.array([0, 16, 64], np.int32), bits=4, codes=FAKE, s=FAKE, z=FAKE)
+             bounds=np.array([0, 16, 64], np.int32), bits=4, codes=FAKE, s=FAKE, z=FAKE, ws=FAKE,
+             ws_bytes=1024 * 2 * 2 * 4)
     a.update(kw)
     return P.lib().rptq_ln_reorder_quant_dynamic(a["x"], a["mode"], a["M"], a["K"], a["gamma"], a["beta"],
                                                  a["eps"], a["R"], _vp(a["bounds"]), a["bounds"].size - 1,
-                                                 a["bits"], a["codes"], a["s"], a["z"], None)
+                                                 a["bits"], a["codes"], a["s"], a["z"], a["ws"], a["ws_bytes"],
+                                                 None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -105,11 +107,18 @@ def _ln_dyn(P, **kw):
     (dict(eps=0.0), -1), (dict(gamma=None), -1), (dict(x=None), -1), (dict(codes=None), -1),
     (dict(s=None), -1), (dict(z=None), -1),
     (dict(K=60, bounds=np.array([0, 16, 60], np.int32)), -2),
-    (dict(x=MISALIGNED), -3), (dict(s=MISALIGNED), -3), (dict(z=MISALIGNED), -3),
+    (dict(ws=None), -1), (dict(ws_bytes=1024 * 2 * 2 * 4 - 1), -1),
+    (dict(x=MISALIGNED), -3), (dict(s=MISALIGNED), -3), (dict(z=MISALIGNED), -3), (dict(ws=MISALIGNED), -3),
 ])
 def test_ln_reorder_quant_dynamic_rejects(P, kw, status):
     assert _ln_dyn(P, **kw) == status
     assert P.lib().rptq_last_error().decode()
+
+
+def test_ln_dynamic_workspace_size(P):
+    # one (lo, hi) pair per cluster for each of at most 1024 workgroups
+    assert [P.rptq_ln_dynamic_workspace_bytes(g) for g in (1, 32, 64)] == [8192, 262144, 524288]
+    assert P.rptq_ln_dynamic_workspace_bytes(0) == -1 and P.rptq_ln_dynamic_workspace_bytes(65) == -1
 
 
 def _gemm_dyn(P, **kw):
