@@ -30,23 +30,6 @@ constexpr int kAttnBlock = 256;
 constexpr int kAttnMaxRounds = 4;          // score tasks per lane: H * D/16 <= 4 * 256
 constexpr int kAttnRing = 4;               // packed rows in flight per workgroup
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Wait until this wave has at most n vector-memory operations pending.
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier for LDS traffic only: this wave's LDS operations are
-// complete, its memory loads may still be in flight (a full __syncthreads
-// would wait for the ring's prefetches too).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
-    __builtin_amdgcn_s_barrier();
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));

@@ -55,6 +55,24 @@ __device__ __forceinline__ uint32_t quant_bits(float v, float inv_s, float zf, f
 }
 
 // Wave64 sum.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Wait until this wave has at most n vector-memory operations pending
+// (loads, including loads that write LDS, and stores complete in issue order).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete, its memory loads may still be in flight (a full __syncthreads
+// would also wait for every prefetch).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
