@@ -400,3 +400,54 @@ def test_calib_minmax_matches_oracle(P):
     mx_o, mn_o = orc.channel_minmax(orc.layernorm(x, gamma, beta))
     np.testing.assert_allclose(mx.cpu().numpy(), mx_o, rtol=2e-5, atol=2e-5)
     np.testing.assert_allclose(mn.cpu().numpy(), mn_o, rtol=2e-5, atol=2e-5)
+
+
+# ----------------------------------------------------------------------------- HIP graphs
+def test_hot_path_replays_from_a_hip_graph(P):
+    """The layer (fused LayerNorm-quant -> GEMM, and the dynamic-range
+    pipeline -> device-scale GEMM) captured once in a HIP graph and replayed
+    several times, with eager work and synchronizations between replays:
+    every replay reproduces the eager results bit for bit (the library
+    records no memset and allocates nothing, so its launches capture as
+    plain kernel nodes)."""
+    M, K, N, g, ab, wb = 96, 2048, 264, 8, 4, 4
+    c = layer_case(M, K, N, g, ab, wb, seed=4242)
+    xd = dev(c.x.view(np.int16)).view(torch.float16)
+    Rd, gr, br = dev(c.R), dev(c.gamma[c.R]), dev(c.beta[c.R])
+    wp, cs, sw = _gemm_inputs(P, c)
+    rb = orc.seg32_row_bytes(c.bounds, ab)
+    codes = torch.empty((M, rb), dtype=torch.uint8, device="cuda")
+    codes_d = torch.empty_like(codes)
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    Yd = torch.empty_like(Y)
+    sd = torch.empty(g, dtype=torch.float32, device="cuda")
+    zd = torch.empty(g, dtype=torch.int32, device="cuda")
+    ws = torch.empty(P.rptq_ln_dynamic_workspace_bytes(g), dtype=torch.uint8, device="cuda")
+
+    def layer():
+        P.rptq_ln_reorder_quant(xd, Rd, gr, br, c.bounds, c.s, c.z, ab, out=codes)
+        P.rptq_qgemm(codes, M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs, out=Y)
+        P.rptq_ln_reorder_quant_dynamic(xd, Rd, gr, br, c.bounds, ab, out=codes_d, s_out=sd, z_out=zd,
+                                        workspace=ws)
+        P.rptq_qgemm_dynamic(codes_d, M, K, N, c.bounds, sd, zd, ab, wp, wb, sw, cs, out=Yd)
+
+    layer()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (codes, Y, codes_d, sd, zd, Yd)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()                                     # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    for rep in range(4):
+        for t in (codes, Y, codes_d, sd, zd, Yd):
+            t.zero_()                               # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip((codes, Y, codes_d, sd, zd, Yd), want):
+            assert torch.equal(got, exp), rep
