@@ -352,3 +352,52 @@ def test_host_helpers_reject(P):
     with pytest.raises(P.RptqError):
         P.rptq_cluster_params(np.zeros(4, np.float32), np.zeros(4, np.float32), None,
                               np.array([0, 2, 2, 4], np.int32), 4)
+
+
+# ----------------------------------------------------------------------------- the ABI from plain C
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "rptq.h"
+
+int main(void) {
+    const int32_t bounds[6] = {0, 1, 32, 64, 97, 192};
+    const float s[2] = {0.1f, 0.2f};
+    const int32_t z[2] = {3, -2};
+    const int32_t b2[3] = {0, 16, 64};
+    int bad = 0;
+    if (rptq_codes_kpad(bounds, 5) != 256) bad |= 1;
+    if (rptq_codes_row_bytes(bounds, 5, 3) != 96) bad |= 2;
+    if (rptq_kv_row_bytes(9216, 3) != 3456) bad |= 4;
+    if (rptq_ln_dynamic_workspace_bytes(32) != 262144) bad |= 8;
+    /* argument errors come back before any HIP call, with a message */
+    if (rptq_ln_reorder_quant(NULL, 0, 4, 64, NULL, NULL, 1e-5f, NULL, b2, 2, s, z, 5, NULL, NULL)
+        != RPTQ_ERR_INVALID_ARG) bad |= 16;
+    if (strlen(rptq_last_error()) == 0) bad |= 32;
+    if (rptq_qgemm(NULL, 0, 64, 32, b2, 2, s, z, 4, NULL, 4, NULL, NULL, NULL, NULL, NULL) != RPTQ_OK) bad |= 64;
+    if (strcmp(rptq_status_string(RPTQ_ERR_ALIGNMENT), rptq_status_string(RPTQ_OK)) == 0) bad |= 128;
+    printf("%s %d\n", rptq_version(), bad);
+    return bad;
+}
+"""
+
+
+def test_abi_from_plain_c(P, tmp_path):
+    """The header compiles as C99 and the library links and runs from a C
+    program (host-side entry points and argument errors only)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(P.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                        "-L", libdir, "-lrptq", "-Wl,-rpath," + libdir, "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.split()[-1] == "0"
