@@ -100,45 +100,106 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
     float gam[UPL][8], bet[UPL][8];
     float uinv[UPL], uzf[UPL];
     int uob[UPL];
+    // every unit's cluster first (no dependent memory access), then the table
+    // loads all at once, then the padding / idle selections as arithmetic on
+    // the loaded values (a select of a loaded value would be turned into a
+    // branch around its load, one load and wait at a time): 1 * x + 0 = x,
+    // 0 * x + kPad = kPad.  A padding or idle position reads a valid index;
+    // gamma 0 and beta kPad decide its code.
+    const LaneClusters lc = lane_clusters(ca, true);
+    int ucl[UPL], up0[UPL];
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) up0[u] = UnitGeom<BITS>::first(tid + u * BLOCK);
+    clusters_of<UPL>(lc, ca.g, up0, ucl);
+    int jb[UPL];                                 // reordered index of element 0
+    float um[UPL][8];                            // 1: real position, 0: padding / idle
 #pragma unroll
     for (int u = 0; u < UPL; ++u) {
         const int unit = tid + u * BLOCK;
+        const bool live = unit < n_units;
+        const int c = ucl[u];
+        // cluster c's entries, fetched by every lane: a crossbar read takes
+        // its value from the source lane only if that lane runs it too, so
+        // none of these sits under a condition
+        const int cb = from_lane(lc.bound, c), co = from_lane(lc.off, c);
+        const int nb = from_lane(lc.bound, c + 1 < ca.g ? c + 1 : c);
+        const int cn = c + 1 < ca.g ? nb : ca.K;
+        const float cinv = from_lane(lc.inv_s, c);
+        const int cz = from_lane(lc.z, c);
         uinv[u] = 0.0f;
         uzf[u] = 0.0f;
-        uob[u] = (int)(dummy - orow);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { src[u][e] = 0; gam[u][e] = 0.0f; bet[u][e] = kPad; }
-        if (unit < n_units) {
-            const int p0 = UnitGeom<BITS>::first(unit);
-            const int c = cluster_of_padded(ca, p0);
-            const int n_c = ca.bounds[c + 1] - ca.bounds[c];
+        if (live) {
             if constexpr (DM == kDevParams) {
                 uinv[u] = 1.0f / dyn_a[c];           // correctly rounded, as on the host
                 uzf[u] = (float)dyn_b[c];
             } else {
-                uinv[u] = ca.inv_s[c];
-                uzf[u] = (float)ca.z[c];           // |z| <= 2^21: exact
-            }
-            uob[u] = UnitGeom<BITS>::out_byte(unit);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int i = p0 + e * UnitGeom<BITS>::stride - ca.off[c];
-                // ranges pass: a padding position repeats the cluster's first
-                // channel, which leaves the cluster's min and max unchanged
-                if (i < n_c || DM == kRanges) {
-                    const int j = ca.bounds[c] + (i < n_c ? i : 0);
-                    if constexpr (LN) {
-                        src[u][e] = (R ? R[j] : j) * 2;
-                        gam[u][e] = gamma_r[j];
-                        bet[u][e] = beta_r[j];
-                    } else {
-                        src[u][e] = j * 4;
-                        gam[u][e] = 1.0f;
-                        bet[u][e] = 0.0f;
-                    }
-                }
+                uinv[u] = cinv;
+                uzf[u] = (float)cz;                  // |z| <= 2^21: exact
             }
         }
+        uob[u] = live ? UnitGeom<BITS>::out_byte(unit) : (int)(dummy - orow);
+        const int i0 = up0[u] - co;                  // >= 0 for a live unit
+        jb[u] = live ? cb + i0 : 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            um[u][e] = live && i0 + e * UnitGeom<BITS>::stride < cn - cb ? 1.0f : 0.0f;
+    }
+    if constexpr (LN) {
+        // indices past K read zeros (range check); a NULL R reads zeros
+        // through a zero-byte descriptor and is replaced by the index itself
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(R, R ? (int64_t)K * 4 : 0);
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(gamma_r, (int64_t)K * 4);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta_r, (int64_t)K * 4);
+        const bool has_r = R != nullptr;
+#pragma unroll
+        for (int u = 0; u < UPL; ++u) {
+            int rv[8];
+            float gv[8], bv[8];
+            if constexpr (UnitGeom<BITS>::stride == 1) {
+                // 8 consecutive indices: two 16-byte loads per table
+                const uint32_t off = (uint32_t)jb[u] * 4u;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4 r4 = __builtin_amdgcn_raw_buffer_load_b128(rr, off + 16 * h, 0, 0);
+                    const u32x4 g4 = __builtin_amdgcn_raw_buffer_load_b128(rg, off + 16 * h, 0, 0);
+                    const u32x4 b4 = __builtin_amdgcn_raw_buffer_load_b128(rb, off + 16 * h, 0, 0);
+                    const uint32_t rs[4] = {r4.x, r4.y, r4.z, r4.w}, gs[4] = {g4.x, g4.y, g4.z, g4.w},
+                                   bs[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        rv[4 * h + k] = (int)rs[k];
+                        gv[4 * h + k] = __builtin_bit_cast(float, gs[k]);
+                        bv[4 * h + k] = __builtin_bit_cast(float, bs[k]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t off = (uint32_t)(jb[u] + e * UnitGeom<BITS>::stride) * 4u;
+                    rv[e] = (int)__builtin_amdgcn_raw_buffer_load_b32(rr, off, 0, 0);
+                    gv[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, off, 0, 0));
+                    bv[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0));
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = jb[u] + e * UnitGeom<BITS>::stride;
+                const int k = j + (has_r ? rv[e] - j : 0);
+                src[u][e] = (k < K ? k : 0) * 2;
+                gam[u][e] = gv[e] * um[u][e];
+                bet[u][e] = __builtin_fmaf(bv[e], um[u][e], um[u][e] != 0.0f ? 0.0f : kPad);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < UPL; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = jb[u] + e * UnitGeom<BITS>::stride;
+                src[u][e] = (j < K ? j : 0) * 4;
+                gam[u][e] = um[u][e];
+                bet[u][e] = um[u][e] != 0.0f ? 0.0f : kPad;
+            }
     }
     const float qhi = kRoundMagic + (float)QMAX;
     [[maybe_unused]] float ulo[UPL], uhi[UPL];
@@ -228,16 +289,17 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
             }
         };
         if constexpr (DM == kRanges) {
-            // running (lo, hi) of every unit over the rows (padding
-            // positions repeat a real channel); rows past M add nothing
+            // running (lo, hi) of every unit over the rows, padding
+            // positions (beta kPad) left out; rows past M add nothing
             if (row < M) {
 #pragma unroll
                 for (int u = 0; u < UPL; ++u)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float y = y_of(u, e);
-                        ulo[u] = __builtin_fminf(ulo[u], y);
-                        uhi[u] = __builtin_fmaxf(uhi[u], y);
+                        const bool pad = bet[u][e] == kPad;
+                        ulo[u] = __builtin_fminf(ulo[u], pad ? __builtin_inff() : y);
+                        uhi[u] = __builtin_fmaxf(uhi[u], pad ? -__builtin_inff() : y);
                     }
             }
             __syncthreads();          // every lane is done with the row and the sums

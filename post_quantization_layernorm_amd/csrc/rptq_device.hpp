@@ -229,6 +229,48 @@ __device__ __forceinline__ void load_unit_at(const unsigned char* p, int (&q)[8]
 }
 
 // Cluster holding reordered (unpadded) position j.
+// Cluster lookups for a kernel's set-up, without chains of dependent loads:
+// lane c (< g) of every wave holds cluster c's table entries (one load per
+// lane, all independent), a position's cluster is the number of later
+// cluster starts at or below it (starts read with v_readlane at a uniform
+// index), and its entries come from lane c over the lane crossbar.
+struct LaneClusters {
+    int start;       // bounds[c] (DENSE positions) or off[c] (SEG32 positions)
+    int bound;       // bounds[c]
+    int off;         // off[c]
+    float inv_s;
+    int z;
+};
+__device__ __forceinline__ LaneClusters lane_clusters(const ClusterArgs& ca, bool seg32) {
+    const int l = threadIdx.x & 63;
+    const int c = l < ca.g ? l : ca.g - 1;
+    LaneClusters t;
+    t.bound = ca.bounds[c];
+    t.off = ca.off[c];
+    t.start = seg32 ? t.off : t.bound;
+    if (l >= ca.g) t.start = 0x7fffffff;
+    t.inv_s = ca.inv_s[c];
+    t.z = ca.z[c];
+    return t;
+}
+// clusters of N positions q[] (same for every lane pattern: any lane values)
+template <int N>
+__device__ __forceinline__ void clusters_of(const LaneClusters& t, int g, const int (&q)[N], int (&c)[N]) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) c[n] = 0;
+    for (int k = 1; k < g; ++k) {
+        const int st = __builtin_amdgcn_readlane(t.start, k);
+#pragma unroll
+        for (int n = 0; n < N; ++n) c[n] += q[n] >= st ? 1 : 0;
+    }
+}
+// (every lane of the wave must execute it: a lane that does not run the
+// crossbar read supplies no value to the lanes that read from it)
+template <class T>
+__device__ __forceinline__ T from_lane(T v, int c) {
+    return __builtin_bit_cast(T, __shfl(__builtin_bit_cast(int, v), c, 64));
+}
+
 __device__ __forceinline__ int cluster_of_pos(const ClusterArgs& ca, int j) {
     int c = 0;
     while (c + 1 < ca.g && j >= ca.bounds[c + 1]) ++c;
