@@ -20,6 +20,57 @@
 namespace rptq {
 namespace {
 
+// Per-lane unit tables of a DENSE row (fixed for every row): for code e of
+// unit u, its natural channel (R[j], j the reordered position) and its
+// cluster's scale entry (1/s or s) and z.  Set-up without dependent-load
+// chains: clusters by counting the cluster starts at or below each position
+// (starts read with v_readlane from a lane-resident table), the cluster
+// entries over the lane crossbar, the R loads all issued together (16-byte
+// loads when a unit's positions are consecutive).  Idle units (unit >=
+// n_units) read position 0; the caller sends them to a dummy slot.
+template <int BITS, int UPL>
+__device__ __forceinline__ void kv_unit_tables(const ClusterArgs& ca, const int32_t* R, int32_t C, int n_units,
+                                               bool want_inv, int (&chan)[UPL][8], float (&sv)[UPL][8],
+                                               int (&zv)[UPL][8]) {
+    const int tid = threadIdx.x, BLOCK = blockDim.x;
+    const LaneClusters lc = lane_clusters(ca, false);
+    const float sl = want_inv ? lc.inv_s : lc.s;
+    int pos[UPL * 8], cl[UPL * 8];
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) {
+        const int unit = tid + u * BLOCK;
+        const int p0 = unit < n_units ? UnitGeom<BITS>::first(unit) : 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pos[u * 8 + e] = p0 + e * UnitGeom<BITS>::stride;
+    }
+    clusters_of<UPL * 8>(lc, ca.g, pos, cl);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(R, R ? (int64_t)C * 4 : 0);
+    const bool has_r = R != nullptr;
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) {
+        int rv[8];
+        if constexpr (UnitGeom<BITS>::stride == 1) {
+            const uint32_t off = (uint32_t)pos[u * 8] * 4u;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 r4 = __builtin_amdgcn_raw_buffer_load_b128(rr, off + 16 * h, 0, 0);
+                rv[4 * h] = (int)r4.x; rv[4 * h + 1] = (int)r4.y; rv[4 * h + 2] = (int)r4.z; rv[4 * h + 3] = (int)r4.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                rv[e] = (int)__builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)pos[u * 8 + e] * 4u, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = pos[u * 8 + e];
+            chan[u][e] = j + (has_r ? rv[e] - j : 0);
+            sv[u][e] = from_lane(sl, cl[u * 8 + e]);
+            zv[u][e] = from_lane(lc.z, cl[u * 8 + e]);
+        }
+    }
+}
+
 template <int BITS, int UPL, bool OVEC16>
 __global__ __launch_bounds__(kMaxBlock) void kv_quant_pack_kernel(
     const uint16_t* __restrict__ kv, int64_t T, int32_t C, const int32_t* __restrict__ R,
@@ -40,21 +91,15 @@ __global__ __launch_bounds__(kMaxBlock) void kv_quant_pack_kernel(
 
     int src[UPL][8], zb[UPL][8], uob[UPL];
     float inv[UPL][8];
+    kv_unit_tables<BITS, UPL>(ca, R, C, n_units, true, src, inv, zb);
 #pragma unroll
     for (int u = 0; u < UPL; ++u) {
         const int unit = tid + u * BLOCK;
-        const bool live = unit < n_units;
-        uob[u] = live ? UnitGeom<BITS>::out_byte(unit) : (int)(dummy - orow);
+        uob[u] = unit < n_units ? UnitGeom<BITS>::out_byte(unit) : (int)(dummy - orow);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            src[u][e] = 0; inv[u][e] = 0.0f; zb[u][e] = 0;
-            if (live) {
-                const int j = UnitGeom<BITS>::first(unit) + e * UnitGeom<BITS>::stride;
-                const int c = cluster_of_pos(ca, j);
-                src[u][e] = (R ? R[j] : j) * 2;
-                inv[u][e] = ca.inv_s[c];
-                zb[u][e] = ca.z[c] - kRoundMagicBits;
-            }
+            src[u][e] *= 2;                          // byte offset of the fp16 input
+            zb[u][e] -= kRoundMagicBits;
         }
     }
 
@@ -111,20 +156,18 @@ __global__ __launch_bounds__(kMaxBlock) void kv_dequant_kernel(
 
     int dst[UPL][8], uib[UPL];
     float sc[UPL][8], zf[UPL][8];
+    {
+        int zi[UPL][8];
+        kv_unit_tables<BITS, UPL>(ca, R, C, n_units, false, dst, sc, zi);
 #pragma unroll
-    for (int u = 0; u < UPL; ++u) {
-        const int unit = tid + u * BLOCK;
-        const bool live = unit < n_units;
-        uib[u] = live ? UnitGeom<BITS>::out_byte(unit) : 0;
+        for (int u = 0; u < UPL; ++u) {
+            const int unit = tid + u * BLOCK;
+            const bool live = unit < n_units;
+            uib[u] = live ? UnitGeom<BITS>::out_byte(unit) : 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            dst[u][e] = (int)(dummy - orow); sc[u][e] = 0.0f; zf[u][e] = 0.0f;
-            if (live) {
-                const int j = UnitGeom<BITS>::first(unit) + e * UnitGeom<BITS>::stride;
-                const int c = cluster_of_pos(ca, j);
-                dst[u][e] = (R ? R[j] : j) * 2;
-                sc[u][e] = ca.s[c];
-                zf[u][e] = (float)ca.z[c];       // |z| <= 2^21: exact
+            for (int e = 0; e < 8; ++e) {
+                dst[u][e] = live ? dst[u][e] * 2 : (int)(dummy - orow);
+                zf[u][e] = (float)zi[u][e];      // |z| <= 2^21: exact
             }
         }
     }

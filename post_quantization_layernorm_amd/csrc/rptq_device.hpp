@@ -239,6 +239,7 @@ struct LaneClusters {
     int bound;       // bounds[c]
     int off;         // off[c]
     float inv_s;
+    float s;
     int z;
 };
 __device__ __forceinline__ LaneClusters lane_clusters(const ClusterArgs& ca, bool seg32) {
@@ -250,6 +251,7 @@ __device__ __forceinline__ LaneClusters lane_clusters(const ClusterArgs& ca, boo
     t.start = seg32 ? t.off : t.bound;
     if (l >= ca.g) t.start = 0x7fffffff;
     t.inv_s = ca.inv_s[c];
+    t.s = ca.s[c];
     t.z = ca.z[c];
     return t;
 }
