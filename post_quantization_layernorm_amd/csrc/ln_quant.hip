@@ -186,8 +186,18 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
                 const int j = jb[u] + e * UnitGeom<BITS>::stride;
                 const int k = j + (has_r ? rv[e] - j : 0);
                 src[u][e] = (k < K ? k : 0) * 2;
-                gam[u][e] = gv[e] * um[u][e];
-                bet[u][e] = __builtin_fmaf(bv[e], um[u][e], um[u][e] != 0.0f ? 0.0f : kPad);
+                if constexpr (DM == kRanges) {
+                    // ranges pass: a padding position repeats element 0 of its
+                    // unit (real whenever the unit has a real position), which
+                    // leaves the unit's min and max unchanged
+                    const float m = um[u][e];
+                    src[u][e] = m != 0.0f ? src[u][e] : src[u][0];
+                    gam[u][e] = __builtin_fmaf(gv[e], m, gv[0] * (1.0f - m));
+                    bet[u][e] = __builtin_fmaf(bv[e], m, bv[0] * (1.0f - m));
+                } else {
+                    gam[u][e] = gv[e] * um[u][e];
+                    bet[u][e] = __builtin_fmaf(bv[e], um[u][e], um[u][e] != 0.0f ? 0.0f : kPad);
+                }
             }
         }
     } else {
@@ -197,10 +207,21 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
             for (int e = 0; e < 8; ++e) {
                 const int j = jb[u] + e * UnitGeom<BITS>::stride;
                 src[u][e] = (j < K ? j : 0) * 4;
-                gam[u][e] = um[u][e];
-                bet[u][e] = um[u][e] != 0.0f ? 0.0f : kPad;
+                if constexpr (DM == kRanges) {
+                    // padding repeats element 0 of the unit (see above)
+                    src[u][e] = um[u][e] != 0.0f ? src[u][e] : src[u][0];
+                    gam[u][e] = 1.0f;
+                    bet[u][e] = 0.0f;
+                } else {
+                    gam[u][e] = um[u][e];
+                    bet[u][e] = um[u][e] != 0.0f ? 0.0f : kPad;
+                }
             }
     }
+    // units holding at least one real position (bit u)
+    uint32_t ureal = 0;
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) ureal |= um[u][0] != 0.0f ? 1u << u : 0u;
     const float qhi = kRoundMagic + (float)QMAX;
     [[maybe_unused]] float ulo[UPL], uhi[UPL];
 #pragma unroll
@@ -289,17 +310,17 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
             }
         };
         if constexpr (DM == kRanges) {
-            // running (lo, hi) of every unit over the rows, padding
-            // positions (beta kPad) left out; rows past M add nothing
+            // running (lo, hi) of every unit over the rows (padding
+            // positions repeat a real one; units without any are reset after
+            // the last row); rows past M add nothing
             if (row < M) {
 #pragma unroll
                 for (int u = 0; u < UPL; ++u)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float y = y_of(u, e);
-                        const bool pad = bet[u][e] == kPad;
-                        ulo[u] = __builtin_fminf(ulo[u], pad ? __builtin_inff() : y);
-                        uhi[u] = __builtin_fmaxf(uhi[u], pad ? -__builtin_inff() : y);
+                        ulo[u] = __builtin_fminf(ulo[u], y);
+                        uhi[u] = __builtin_fmaxf(uhi[u], y);
                     }
             }
             __syncthreads();          // every lane is done with the row and the sums
@@ -336,10 +357,12 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
     if constexpr (DM == kRanges) {
         // units -> 32-code groups (4 consecutive units in 4 consecutive
         // lanes) -> clusters (one wave per cluster at a time) -> this
-        // workgroup's (lo, hi) per cluster
+        // workgroup's (lo, hi) per cluster; a unit without a real position
+        // (idle, or all padding) takes no part
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
-            float lo = ulo[u], hi = uhi[u];
+            const bool none = !(ureal >> u & 1u);
+            float lo = none ? __builtin_inff() : ulo[u], hi = none ? -__builtin_inff() : uhi[u];
             lo = __builtin_fminf(lo, __shfl_xor(lo, 1, 64));
             hi = __builtin_fmaxf(hi, __shfl_xor(hi, 1, 64));
             lo = __builtin_fminf(lo, __shfl_xor(lo, 2, 64));
