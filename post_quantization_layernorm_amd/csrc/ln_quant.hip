@@ -126,16 +126,15 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
         const int cn = c + 1 < ca.g ? nb : ca.K;
         const float cinv = from_lane(lc.inv_s, c);
         const int cz = from_lane(lc.z, c);
-        uinv[u] = 0.0f;
-        uzf[u] = 0.0f;
-        if (live) {
-            if constexpr (DM == kDevParams) {
-                uinv[u] = 1.0f / dyn_a[c];           // correctly rounded, as on the host
-                uzf[u] = (float)dyn_b[c];
-            } else {
-                uinv[u] = cinv;
-                uzf[u] = (float)cz;                  // |z| <= 2^21: exact
-            }
+        if constexpr (DM == kDevParams) {
+            // (loaded for every lane: c is a valid cluster for idle units too)
+            const float ds = dyn_a[c];
+            const int dz = dyn_b[c];
+            uinv[u] = live ? 1.0f / ds : 0.0f;       // correctly rounded, as on the host
+            uzf[u] = live ? (float)dz : 0.0f;
+        } else {
+            uinv[u] = live ? cinv : 0.0f;
+            uzf[u] = live ? (float)cz : 0.0f;        // |z| <= 2^21: exact
         }
         uob[u] = live ? UnitGeom<BITS>::out_byte(unit) : (int)(dummy - orow);
         const int i0 = up0[u] - co;                  // >= 0 for a live unit
@@ -151,6 +150,17 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
         const __amdgpu_buffer_rsrc_t rg = make_rsrc(gamma_r, (int64_t)K * 4);
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta_r, (int64_t)K * 4);
         const bool has_r = R != nullptr;
+        if constexpr (UnitGeom<BITS>::stride != 1) {
+#pragma unroll
+            for (int u = 0; u < UPL; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t off = (uint32_t)(jb[u] + e * UnitGeom<BITS>::stride) * 4u;
+                    src[u][e] = (int)__builtin_amdgcn_raw_buffer_load_b32(rr, off, 0, 0);
+                    gam[u][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, off, 0, 0));
+                    bet[u][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0));
+                }
+        }
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
             int rv[8];
@@ -173,13 +183,10 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
                     }
                 }
             } else {
+                // strided positions: one load per position and table, issued
+                // for every unit before the first is used (below)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t off = (uint32_t)(jb[u] + e * UnitGeom<BITS>::stride) * 4u;
-                    rv[e] = (int)__builtin_amdgcn_raw_buffer_load_b32(rr, off, 0, 0);
-                    gv[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, off, 0, 0));
-                    bv[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0));
-                }
+                for (int e = 0; e < 8; ++e) { rv[e] = src[u][e]; gv[e] = gam[u][e]; bv[e] = bet[u][e]; }
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
