@@ -451,3 +451,58 @@ def test_hot_path_replays_from_a_hip_graph(P):
         torch.cuda.synchronize()
         for got, exp in zip((codes, Y, codes_d, sd, zd, Yd), want):
             assert torch.equal(got, exp), rep
+
+
+# ----------------------------------------------------------------------------- smallest shapes
+@pytest.mark.parametrize("bits", [3, 4, 8])
+@pytest.mark.parametrize("bounds", [[0, 8], [0, 1, 2, 3, 4, 5, 6, 7, 8], [0, 3, 8]], ids=["g1", "g8", "g2"])
+def test_smallest_layer(P, bits, bounds):
+    """K = 8 (one 8-code unit of real channels), every cluster padded to 32:
+    LayerNorm-quant (fused within tolerance, quant-only and dynamic bit
+    exact), the GEMM (accumulators exact) and the dynamic-range GEMM."""
+    M, K, N = 5, 8, 24
+    _say("smallest", bits, bounds)
+    c = explicit_case(M, K, N, bounds, bits, 4, seed=len(bounds) + bits)
+    y = orc.layernorm(c.x, c.gamma, c.beta, 1e-5, c.R)
+    want = orc.pack_seg32(orc.quantize(y, c.bounds, c.s, c.z, bits), c.bounds, bits)
+    got = P.rptq_ln_reorder_quant(dev(y), None, None, None, c.bounds, c.s, c.z, bits,
+                                  in_mode=P.RPTQ_IN_FP32_NORMALIZED)
+    assert np.array_equal(got.cpu().numpy(), want)
+    wd, sd_o, zd_o = orc.quantize_dynamic(y, c.bounds, bits)
+    gd, sd, zd = P.rptq_ln_reorder_quant_dynamic(dev(y), None, None, None, c.bounds, bits,
+                                                 in_mode=P.RPTQ_IN_FP32_NORMALIZED)
+    assert np.array_equal(gd.cpu().numpy(), wd)
+    assert np.array_equal(sd.cpu().numpy(), sd_o) and np.array_equal(zd.cpu().numpy(), zd_o)
+    fused = _fused(P, c, bits).cpu().numpy()
+    qf = orc.unpack_seg32(fused, K, c.bounds, bits).astype(np.int32)
+    qo = orc.unpack_seg32(orc.ln_reorder_quant(c.x, c.gamma, c.beta, 1e-5, c.R, c.bounds, c.s, c.z, bits),
+                          K, c.bounds, bits).astype(np.int32)
+    assert np.abs(qf - qo).max() <= 1
+    q = orc.unpack_seg32(want, K, c.bounds, bits)
+    Y_o, acc_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w, return_acc=True)
+    wp, cs, sw = _gemm_inputs(P, c)
+    acc = torch.zeros((c.g, M, N), dtype=torch.int32, device="cuda")
+    Y = P.rptq_qgemm(dev(want), M, K, N, c.bounds, c.s, c.z, bits, wp, 4, sw, cs, acc_debug=acc)
+    assert np.array_equal(acc.cpu().numpy(), acc_o)
+    assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
+    Yd = P.rptq_qgemm_dynamic(gd, M, K, N, c.bounds, sd, zd, bits, wp, 4, sw, cs)
+    Ys = P.rptq_qgemm(gd, M, K, N, c.bounds, sd.cpu().numpy(), zd.cpu().numpy(), bits, wp, 4, sw, cs)
+    assert torch.equal(Yd, Ys)
+
+
+@pytest.mark.parametrize("bits,C", [(4, 8), (8, 8), (3, 32), (4, 32)])
+def test_smallest_kv_rows(P, bits, C):
+    """The narrowest K/V rows (C = 8, 3-bit C = 32), single-channel clusters
+    included: pack and dequant bit-exact."""
+    T = 7
+    r = np.random.default_rng(C + bits)
+    kv = (r.standard_normal((T, C)) * 3).astype(np.float16)
+    bounds = np.array(sorted({0, C} | {int(v) for v in r.integers(1, C, 3)}), np.int32)
+    R = r.permutation(C).astype(np.int32)
+    mx, mn = orc.channel_minmax(kv)
+    s, z = orc.cluster_params(mx, mn, R, bounds, bits)
+    want = orc.kv_quant_pack(kv, R, bounds, s, z, bits)
+    got = P.rptq_kv_quant_pack(dev(kv.view(np.int16)).view(torch.float16), dev(R), bounds, s, z, bits)
+    assert np.array_equal(got.cpu().numpy(), want)
+    deq = P.rptq_kv_dequant(dev(want), C, dev(R), bounds, s, z, bits)
+    assert np.array_equal(deq.cpu().numpy().view(np.uint16), orc.kv_dequant(want, C, R, bounds, s, z, bits))
