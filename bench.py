@@ -66,10 +66,10 @@ KERNEL_SOURCES = {
 }
 
 
-def measured_traffic(kernel: str, launches_bytes: float):
+def measured_traffic(kernel: str, launches_bytes: float, path=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path)).get(kernel)
@@ -396,7 +396,7 @@ def _pmc_per_dispatch(path, counter):
     return out
 
 
-def ingest_pmc(fetch_csv, write_csv):
+def ingest_pmc(fetch_csv, write_csv, out_path=None):
     """HBM bytes per launch = FETCH_SIZE + WRITE_SIZE (KiB per dispatch), each
     scaled so that the copy probe (the last copy dispatch of the run) reads
     and writes exactly COPY_PROBE_BYTES."""
@@ -425,10 +425,11 @@ def ingest_pmc(fetch_csv, write_csv):
                         "fetch_bytes": vals["FETCH_SIZE"], "write_bytes": vals["WRITE_SIZE"],
                         "scale_fetch": scale["FETCH_SIZE"], "scale_write": scale["WRITE_SIZE"],
                         "kernel_match": pat}
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = out_path or os.path.join(ROOT, "profiles", "hbm_traffic.json")
     with open(path, "w") as fh:
         json.dump(res, fh, indent=1, sort_keys=True)
     print(json.dumps(res, indent=1))
+    return res
 
 
 def cpu_baseline(w, x_dev, gamma, beta, R, bounds, s, z, N, budget_s):
