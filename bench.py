@@ -321,6 +321,11 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": elapsed / args.steps * 1e3,
+        # value is the W4A4 LayerNorm-quant -> GEMM pair alone; a step also
+        # runs the other layer variants and the K/V kernels, so M per step
+        # over the whole step is a different (smaller) figure
+        "value_basis": "M / (t_LN + t_GEMM) of the W4A4 pair; ms_per_step covers every kernel of the step",
+        "step_tokens_per_s": M / (elapsed / args.steps),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic (seeded per-channel N(mu_c, sigma_c) activations with 1% x100 outlier channels; "
