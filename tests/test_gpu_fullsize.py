@@ -1,7 +1,8 @@
-"""GPU parity at the full benchmark sizes, in the launch configurations the
+"""GPU parity at the full workload sizes, in the launch configurations the
 benchmark times: the OPT-66B fc1 layer (16384 tokens x 9216 -> 36864, g = 32,
-W4A4, W4A3 and W3A3) and the OPT-66B K/V cache (524288 tokens x 9216 channels,
-3 bit).  The device runs every row; the oracle checks sampled rows one by one
+W4A4, W4A3 and W3A3), the OPT-66B K/V cache (524288 tokens x 9216 channels,
+3 bit), and the three smaller layers (OPT-125m W8A8, OPT-1.3B fc1 W4A4,
+OPT-13B QKV W4A4 / W4A8).  The device runs every row; the oracle checks sampled rows one by one
 (its cost grows with the sample, not with the launch).  All parameters (R,
 bounds, s, z, Wq) come from the oracle's calibration."""
 import numpy as np
@@ -186,3 +187,58 @@ def test_kv_attention_fullsize_sampled(P):
                   for r, par in zip(raw, params))
         want = orc.kv_attention(q[b:b + 1], kp, vp, 1, Ts, C, D, 1.0 / np.sqrt(D), params[0], params[1], bits)
         assert rel_l2(got[b], want[0]) <= 1e-3, (b, rel_l2(got[b], want[0]))
+
+
+# ----------------------------------------------------------------------------- the three smaller layers
+SMALLER = [("opt125m_w8a8", 8), ("opt1.3b_fc1_w4a4", 4), ("opt13b_qkv_w4a4", 4), ("opt13b_qkv_w4a4", 8)]
+
+
+@pytest.mark.parametrize("name,ab", SMALLER, ids=[f"{n}-A{a}" for n, a in SMALLER])
+def test_layer_fullsize_sampled(P, name, ab):
+    """The OPT-125m layer (W8A8), the OPT-1.3B fc1 (W4A4) and the OPT-13B
+    QKV projection (W4A4 and W4A8, 10x-300x channel ranges) at their full
+    sizes: the fused LayerNorm kernel over every row (sampled rows within the
+    code tolerance), the GEMM over every row on the oracle's codes (sampled
+    rows of Y within 1e-3, and the int32 accumulators of a 64-row slice bit
+    exact over full K and N)."""
+    w = synthetic.WORKLOADS[name]
+    M, K, N, g, wb = w.M, w.K, w.N, w.g, w.w_bits
+    _say("layer", name, ab, M, K, N)
+    mu, sg = synthetic.channel_params(K, w.seed, w.outlier_frac, range_ratio=w.range_ratio)
+    gamma, beta = synthetic.ln_params(K, w.seed, random=True)
+    xc = synthetic.tokens(w.calib_tokens, mu, sg, w.seed, synthetic.STREAM_CALIB)
+    mx, mn = orc.channel_minmax(orc.layernorm(xc, gamma, beta))
+    R, bounds, s, z = orc.calibrate(mx, mn, g, ab, synthetic.kmeans_uniforms(w.seed, 3, g), n_init=3)
+    x = synthetic.tokens(M, mu, sg, w.seed, synthetic.STREAM_EVAL)
+    Wq, s_w = orc.quantize_weights(synthetic.weights(K, N, w.seed), wb)
+    rows = np.unique(np.array([0, 1, M // 2 - 1, M // 2, M - 2, M - 1]))
+
+    # fused LayerNorm + reorder + quantize + pack over every row
+    xd = dev(x.view(np.int16)).view(torch.float16)
+    codes = P.rptq_ln_reorder_quant(xd, dev(R), dev(gamma[R]), dev(beta[R]), bounds, s, z, ab)
+    got = codes[torch.from_numpy(rows).cuda()].cpu().numpy()
+    codes_o = orc.ln_reorder_quant(x, gamma, beta, 1e-5, R, bounds, s, z, ab)
+    qg, pad = orc.unpack_seg32(got, K, bounds, ab, return_pad=True)
+    qw = orc.unpack_seg32(codes_o[rows], K, bounds, ab)
+    d = np.abs(qg.astype(np.int32) - qw.astype(np.int32))
+    assert not pad.any()
+    assert d.max() <= 1 and (d > 0).mean() <= 1e-3, (d.max(), (d > 0).mean())
+    del codes
+
+    # the GEMM over every row, on the oracle's codes
+    wp, cs = P.rptq_pack_weights(Wq, R, bounds, wb)
+    wp, cs, sw = dev(wp), dev(cs), dev(s_w)
+    cd = dev(codes_o)
+    Y = P.rptq_qgemm(cd, M, K, N, bounds, s, z, ab, wp, wb, sw, cs)
+    Ys = Y[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del Y
+    Y_o = orc.qgemm(orc.unpack_seg32(codes_o[rows], K, bounds, ab), Wq, R, bounds, s, z, s_w)
+    for i in range(len(rows)):
+        assert rel_l2(Ys[i], Y_o[i]) <= 1e-3, rows[i]
+    r0 = max(0, M // 2 - 32)
+    n64 = min(64, M - r0)
+    acc = torch.zeros((g, n64, N), dtype=torch.int32, device="cuda")
+    P.rptq_qgemm(cd[r0:r0 + n64], n64, K, N, bounds, s, z, ab, wp, wb, sw, cs, acc_debug=acc)
+    _, acc_o = orc.qgemm(orc.unpack_seg32(codes_o[r0:r0 + n64], K, bounds, ab), Wq, R, bounds, s, z, s_w,
+                         return_acc=True)
+    assert np.array_equal(acc.cpu().numpy(), acc_o)
