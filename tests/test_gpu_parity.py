@@ -453,6 +453,52 @@ def test_hot_path_replays_from_a_hip_graph(P):
             assert torch.equal(got, exp), rep
 
 
+def test_kv_path_replays_from_a_hip_graph(P):
+    """K/V pack, dequantize and decode attention (tables, chunk and merge
+    kernels) captured once in a HIP graph and replayed with eager work
+    between replays: every replay equals the eager results bit for bit."""
+    B, T, C, D, g, bits = 2, 300, 1024, 128, 8, 3
+    (kp, kpar), (vp, vpar) = _attn_inputs(B, T, C, g, bits, seed=77)
+    R, bounds, s, z = kpar
+    kv = orc.half_to_double(orc.kv_dequant(kp, C, R, bounds, s, z, bits)).astype(np.float16)
+    kvd = dev(kv.view(np.int16)).view(torch.float16)
+    q = (np.random.default_rng(5).standard_normal((B, C)) * 0.25).astype(np.float16)
+    qd = dev(q.view(np.int16)).view(torch.float16)
+    dp = lambda par: (dev(par[0]), par[1], par[2], par[3])
+    kpar_d, vpar_d = dp(kpar), dp(vpar)
+    kpd, vpd = dev(kp), dev(vp)
+    packed = torch.empty((B * T, P.rptq_kv_row_bytes(C, bits)), dtype=torch.uint8, device="cuda")
+    deq = torch.empty((B * T, C), dtype=torch.float16, device="cuda")
+    att = torch.empty((B, C), dtype=torch.float32, device="cuda")
+    ws = torch.empty(P.rptq_kv_attention_workspace_bytes(B, T, C, D), dtype=torch.uint8, device="cuda")
+
+    def path():
+        P.rptq_kv_quant_pack(kvd, kpar_d[0], bounds, s, z, bits, out=packed)
+        P.rptq_kv_dequant(packed, C, kpar_d[0], bounds, s, z, bits, out=deq)
+        P.rptq_kv_attention(qd, kpd, vpd, B, T, C, D, 0.125, kpar_d, vpar_d, bits, out=att, workspace=ws)
+
+    path()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (packed, deq, att)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        path()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    for rep in range(4):
+        for t in (packed, deq, att):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip((packed, deq, att), want):
+            assert torch.equal(got, exp), rep
+
+
 # ----------------------------------------------------------------------------- smallest shapes
 @pytest.mark.parametrize("bits", [3, 4, 8])
 @pytest.mark.parametrize("bounds", [[0, 8], [0, 1, 2, 3, 4, 5, 6, 7, 8], [0, 3, 8]], ids=["g1", "g8", "g2"])
