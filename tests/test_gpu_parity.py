@@ -256,6 +256,9 @@ GEMM_CASES = [  # (M, K, N, g, a_bits, w_bits)
     (64, 9216, 136, 32, 3, 3),          # OPT-66B-shaped W3A3 (the write-up's W3A3KV setting)
     (70, 2048, 392, 8, 4, 3),           # W3A4, ragged M and N
     (40, 768, 200, 4, 8, 3),            # W3A8
+    (77, 512, 101, 4, 4, 4),            # odd N: a ragged last column tile
+    (3, 768, 1, 2, 8, 8),               # N = 1
+    (130, 40, 33, 2, 3, 3),             # K = 40 (two clusters padded to 64 codes), odd N
 ]
 
 
