@@ -197,6 +197,41 @@ def test_layernorm_identity_params_match_textbook_numpy(orc):
     assert np.abs(y.astype(np.float64).mean(1)).max() < 1e-5
 
 
+def test_layernorm_random_affine_matches_textbook_numpy(orc):
+    """gamma and beta away from (1, 0): y = gamma * (x - mean) / sqrt(var + eps)
+    + beta against a plain fp64 numpy LayerNorm, in natural and in reordered
+    order (RPTQ write-up, method section and Fig. 3: the LayerNorm emits
+    reordered activations with reordered gamma and beta).  Dropping beta,
+    dividing by gamma or indexing gamma without R each fail here."""
+    K = 320
+    x = _x_small(40, K, seed=5)
+    gamma, beta = synthetic.ln_params(K, 17)
+    assert np.abs(beta).max() > 0.1 and np.abs(gamma - 1).max() > 0.1
+    xd = x.astype(np.float64)
+    mu = xd.mean(1, keepdims=True)
+    var = ((xd - mu) ** 2).mean(1, keepdims=True)
+    ref = gamma.astype(np.float64) * (xd - mu) / np.sqrt(var + 1e-5) + beta.astype(np.float64)
+    y = orc.layernorm(x, gamma, beta, 1e-5)
+    np.testing.assert_allclose(y, ref, rtol=2e-7, atol=2e-7)
+    R = np.random.default_rng(8).permutation(K).astype(np.int32)
+    np.testing.assert_allclose(orc.layernorm(x, gamma, beta, 1e-5, R), ref[:, R], rtol=2e-7, atol=2e-7)
+
+
+def test_layernorm_hand_worked_example(orc):
+    """Four channels worked by hand (tests/golden/layernorm_hand_example.json):
+    mean 2, variance 1, eps 3, so the normalizer is exactly 1/2 and every
+    output is exact in fp32."""
+    ex = json.load(open(os.path.join(GOLDEN, "layernorm_hand_example.json")))
+    x = np.array([ex["x"]], np.float16)
+    gamma = np.array(ex["gamma"], np.float32)
+    beta = np.array(ex["beta"], np.float32)
+    R = np.array(ex["R"], np.int32)
+    y = orc.layernorm(x, gamma, beta, ex["eps"])
+    assert y[0].tolist() == ex["y_natural"]
+    yr = orc.layernorm(x, gamma, beta, ex["eps"], R)
+    assert yr[0].tolist() == ex["y_reordered"]
+
+
 def test_layernorm_reordered_params_equal_permuted_output(orc):
     """LN(x; gamma, beta)[R] == LN(x[R]; gamma[R], beta[R])."""
     K = 384
@@ -532,6 +567,93 @@ def test_kv_round_trip_error_and_natural_order(orc, bits):
     q = orc.unpack_dense(packed, C, bits)
     q2 = orc.quantize(np.ascontiguousarray(kv[:, R].astype(np.float32)), bounds, s, z, bits)
     assert np.array_equal(q, q2)
+
+
+def _double_rounding_cases(count):
+    """(s, n) pairs, s fp32 and n = q - z a small integer, whose exact product
+    s * n lies just off a midpoint of two fp16 neighbours while its fp32
+    rounding lands exactly on that midpoint: rounding the exact value once to
+    fp16 and rounding it to fp32 first give different fp16 results."""
+    cases = []
+    for n in (3, 5, 7, -3, -6, 11):
+        for base in (0.75, 1.0, 3.0, 100.0, -2.0 ** -16):
+            h = np.float16(abs(base))
+            ulp = float(np.spacing(h))
+            for k in range(4):
+                s0 = np.float32((float(h) + (k + 0.5) * ulp) / abs(n))
+                for d in (-2, -1, 1, 2):
+                    s_ = s0
+                    for _ in range(abs(d)):
+                        s_ = np.nextafter(s_, np.float32(np.inf) if d > 0 else np.float32(0))
+                    v = float(s_) * n
+                    if np.float16(v) != np.float16(np.float32(v)):
+                        cases.append((s_, n))
+    assert len(cases) >= count
+    return cases[::max(1, len(cases) // count)][:count]
+
+
+def test_kv_dequant_rounds_the_exact_product_once(orc):
+    """Dequantization W = S (Wq - Z) (quantization lecture, 1.3) with the
+    product formed exactly and rounded once to fp16, the plainest reading of a
+    formula that names no intermediate precision: the oracle's fp16 outputs
+    equal numpy's direct float64 -> float16 conversion (a library routine,
+    round to nearest even) of s * (q - z) on cases built so that rounding to
+    fp32 first would give the other fp16 neighbour."""
+    cases = _double_rounding_cases(8)
+    C = len(cases)                       # one channel per cluster, 4-bit codes
+    bounds = np.arange(C + 1, dtype=np.int32)
+    s = np.array([c[0] for c in cases], np.float32)
+    q = np.array([[5, 9, 1, 15, 0, 7, 12, 3]], np.uint8)[:, :C]
+    z = (q[0].astype(np.int32) - np.array([c[1] for c in cases], np.int32)).astype(np.int32)
+    packed = orc.pack_dense(q, 4)
+    out = orc.kv_dequant(packed, C, None, bounds, s, z, 4).view(np.float16)[0]
+    exact = s.astype(np.float64) * (q[0].astype(np.int64) - z)
+    once = exact.astype(np.float16)
+    twice = exact.astype(np.float32).astype(np.float16)
+    assert (once != twice).all()         # every case separates the two readings
+    assert np.array_equal(out.view(np.uint16), once.view(np.uint16))
+
+
+def test_kv_attention_two_token_closed_form(orc):
+    """Two cached tokens: softmax over two scores is a logistic function, so
+    out = V0 + (V1 - V0) * sigmoid(scale * q . (K1 - K0)) per head, over the
+    dequantized cache.  A moderate, non-power-of-two scale keeps both weights
+    well inside (0, 1), so a squared or doubly applied scale fails; doubling
+    the scale moves the output exactly as the closed form predicts."""
+    B, T, C, D, bits = 3, 2, 64, 32, 4
+    (kp, vp), (kpar, vpar) = _attn_case(orc, B, T, C, bits, 43)
+    K = orc.half_to_double(orc.kv_dequant(kp, C, *kpar, bits)).reshape(B, T, C)
+    V = orc.half_to_double(orc.kv_dequant(vp, C, *vpar, bits)).reshape(B, T, C)
+    rng = np.random.default_rng(4)
+    q = np.empty((B, C), np.float16)
+    for b in range(B):
+        for h in range(C // D):
+            sl = slice(h * D, (h + 1) * D)
+            dk = K[b, 1, sl] - K[b, 0, sl]
+            # a query whose margin q . (K1 - K0) is 5 (1.5 at scale 0.3), plus
+            # a component orthogonal to K1 - K0 that changes no score gap
+            nrm = np.sqrt(np.dot(dk, dk))
+            noise = rng.standard_normal(D)
+            noise -= np.dot(noise, dk) / nrm ** 2 * dk
+            v = dk / nrm ** 2 * 5.0 + noise / np.sqrt(D) * (2.0 / nrm)
+            q[b, sl] = v.astype(np.float16)
+    qd = q.astype(np.float64)
+
+    def closed(scale):
+        out = np.empty((B, C))
+        for b in range(B):
+            for h in range(C // D):
+                sl = slice(h * D, (h + 1) * D)
+                a = scale * np.dot(qd[b, sl], K[b, 1, sl] - K[b, 0, sl])
+                w1 = 1.0 / (1.0 + np.exp(-a))
+                assert 0.05 < w1 < 0.95 or scale != 0.3
+                out[b, sl] = V[b, 0, sl] + (V[b, 1, sl] - V[b, 0, sl]) * w1
+        return out
+
+    for scale in (0.3, 0.6):
+        got = orc.kv_attention(q, kp, vp, B, T, C, D, scale, kpar, vpar, bits)
+        np.testing.assert_allclose(got, closed(scale), rtol=1e-12, atol=1e-12)
+    assert np.abs(closed(0.3) - closed(0.09)).max() > 1e-2       # scale^2 would be caught
 
 
 # ----------------------------------------------------------------------------- dynamic ranges
