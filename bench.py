@@ -89,9 +89,15 @@ def main():
                     help="after the timed region, run one plain device copy of COPY_PROBE_BYTES")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="print per-dispatch counters and derived rates (MFMA busy, clock, LDS activity) "
+                         "from rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(*args.ingest_pmc)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -435,6 +441,50 @@ def ingest_pmc(fetch_csv, write_csv, out_path=None):
         json.dump(res, fh, indent=1, sort_keys=True)
     print(json.dumps(res, indent=1))
     return res
+
+
+N_XCD, N_CU, N_SIMD = 8, 256, 1024      # MI355X
+
+
+def summarize_pmc(paths):
+    """Per dispatch (kernel, grid): duration, every counter summed over its
+    instances, and the derived rates.  GRBM_GUI_ACTIVE is reported summed
+    over the 8 XCDs, so one XCD's active cycles are a 1/8 share; MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x active cycles); the clock is active
+    cycles over the dispatch's duration; LDS active = SQ_LDS_IDX_ACTIVE /
+    (CUs x active cycles); MFMA ops = SQ_INSTS_VALU_MFMA_MOPS_I8 x 512."""
+    import csv
+    from collections import OrderedDict, defaultdict
+    rows = []
+    for path in paths:
+        per = OrderedDict()
+        for r in csv.DictReader(open(path, newline="")):
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]))
+            d = per.setdefault(key, {"dur_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                                     "vgpr": r.get("VGPR_Count"), "agpr": r.get("Accum_VGPR_Count"),
+                                     "lds": r.get("LDS_Block_Size"), "c": defaultdict(float)})
+            d["c"][r["Counter_Name"]] += float(r["Counter_Value"])
+        for (disp, name, grid), d in per.items():
+            c = d["c"]
+            out = {"file": os.path.basename(path), "dispatch": disp, "kernel": name.split("(")[0],
+                   "grid_threads": grid, "dur_us": d["dur_ns"] / 1e3, "counters": dict(c)}
+            if "GRBM_GUI_ACTIVE" in c:
+                cyc = c["GRBM_GUI_ACTIVE"] / N_XCD
+                out["active_cycles_per_xcd"] = cyc
+                out["clock_GHz"] = cyc / d["dur_ns"]
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                    out["mfma_busy_frac"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc)
+                if "SQ_LDS_IDX_ACTIVE" in c:
+                    out["lds_active_frac"] = c["SQ_LDS_IDX_ACTIVE"] / (N_CU * cyc)
+            if "SQ_LDS_IDX_ACTIVE" in c and "SQ_LDS_BANK_CONFLICT" in c and c["SQ_LDS_IDX_ACTIVE"]:
+                out["lds_conflict_frac_of_active"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
+            if "SQ_INSTS_VALU_MFMA_MOPS_I8" in c:
+                out["mfma_int8_ops"] = c["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512
+            if "SQ_ACTIVE_INST_VALU" in c and "SQ_WAVE_CYCLES" in c and c["SQ_WAVE_CYCLES"]:
+                out["valu_active_frac_of_wave_cycles"] = c["SQ_ACTIVE_INST_VALU"] / c["SQ_WAVE_CYCLES"]
+            rows.append(out)
+            print(json.dumps(out))
+    return rows
 
 
 def cpu_baseline(w, x_dev, gamma, beta, R, bounds, s, z, N, budget_s):

@@ -141,6 +141,16 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _empty(shape, dtype, device, stream):
+    """A device tensor allocated on the stream the library call will run on
+    (the caching allocator then never hands its memory to other work while
+    that stream may still use it)."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 # ---------------------------------------------------------------------------- sizes
 def rptq_codes_kpad(bounds) -> int:
     b = _h(bounds, np.int32)
@@ -176,7 +186,7 @@ def rptq_ln_reorder_quant(x, R, gamma_r, beta_r, bounds, s, z, bits, eps=1e-5,
     if rb < 0:
         _check(RPTQ_ERR_INVALID_ARG, "rptq_codes_row_bytes")
     if out is None:
-        out = torch.empty((M, rb), dtype=torch.uint8, device=x.device)
+        out = _empty((M, rb), torch.uint8, x.device, stream)
     st = lib().rptq_ln_reorder_quant(_dp(x), in_mode, M, K, _dp(gamma_r), _dp(beta_r), eps, _dp(R),
                                      _hp(b), b.size - 1, _hp(sh), _hp(zh), bits, _dp(out), _stream(stream))
     _check(st, "rptq_ln_reorder_quant")
@@ -200,13 +210,13 @@ def rptq_ln_reorder_quant_dynamic(x, R, gamma_r, beta_r, bounds, bits, eps=1e-5,
     if rb < 0:
         _check(RPTQ_ERR_INVALID_ARG, "rptq_codes_row_bytes")
     if out is None:
-        out = torch.empty((M, rb), dtype=torch.uint8, device=x.device)
+        out = _empty((M, rb), torch.uint8, x.device, stream)
     if s_out is None:
-        s_out = torch.empty(max(g, 1), dtype=torch.float32, device=x.device)
+        s_out = _empty(max(g, 1), torch.float32, x.device, stream)
     if z_out is None:
-        z_out = torch.empty(max(g, 1), dtype=torch.int32, device=x.device)
+        z_out = _empty(max(g, 1), torch.int32, x.device, stream)
     if workspace is None:
-        workspace = torch.empty(max(rptq_ln_dynamic_workspace_bytes(g), 16), dtype=torch.uint8, device=x.device)
+        workspace = _empty(max(rptq_ln_dynamic_workspace_bytes(g), 16), torch.uint8, x.device, stream)
     st = lib().rptq_ln_reorder_quant_dynamic(_dp(x), in_mode, M, K, _dp(gamma_r), _dp(beta_r), eps, _dp(R),
                                              _hp(b), g, bits, _dp(out), _dp(s_out), _dp(z_out), _dp(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream))
@@ -219,7 +229,7 @@ def rptq_qgemm_dynamic(codes, M, K, N, bounds, s_dev, z_dev, a_bits, w_packed, w
     """rptq_qgemm with (s, z) as cuda tensors (fp32 [g], int32 [g])."""
     b = _h(bounds, np.int32)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+        out = _empty((M, N), torch.float32, codes.device, stream)
     st = lib().rptq_qgemm_dynamic(_dp(codes), M, K, N, _hp(b), b.size - 1, _dp(s_dev), _dp(z_dev), a_bits,
                                   _dp(w_packed), w_bits, _dp(s_w), _dp(colsum), _dp(out), _stream(stream))
     _check(st, "rptq_qgemm_dynamic")
@@ -232,7 +242,7 @@ def rptq_qgemm(codes, M, K, N, bounds, s, z, a_bits, w_packed, w_bits, s_w, cols
     s_w: cuda fp32 [N]; colsum: cuda int32 [g][N].  Returns Y cuda fp32 [M][N]."""
     b = _h(bounds, np.int32); sh = _h(s, np.float32); zh = _h(z, np.int32)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+        out = _empty((M, N), torch.float32, codes.device, stream)
     st = lib().rptq_qgemm(_dp(codes), M, K, N, _hp(b), b.size - 1, _hp(sh), _hp(zh), a_bits, _dp(w_packed),
                           w_bits, _dp(s_w), _dp(colsum), _dp(out), _dp(acc_debug), _stream(stream))
     _check(st, "rptq_qgemm")
@@ -251,7 +261,7 @@ def rptq_qgemm_quant(codes, M, K, N_pad, bounds, s, z, a_bits, w_packed, w_bits,
         rb = rptq_codes_row_bytes(ob, out_bits)
         if rb < 0:
             _check(RPTQ_ERR_INVALID_ARG, "rptq_codes_row_bytes")
-        out = torch.empty((M, rb), dtype=torch.uint8, device=codes.device)
+        out = _empty((M, rb), torch.uint8, codes.device, stream)
     st = lib().rptq_qgemm_quant(_dp(codes), M, K, N_pad, _hp(b), b.size - 1, _hp(sh), _hp(zh), a_bits,
                                 _dp(w_packed), w_bits, _dp(s_w), _dp(colsum), act, _hp(ob), ob.size - 1,
                                 _hp(osh), _hp(ozh), out_bits, _dp(out), _dp(y_out), _stream(stream))
@@ -267,7 +277,7 @@ def rptq_kv_quant_pack(kv, R, bounds, s, z, bits, out=None, stream=None):
         rb = rptq_kv_row_bytes(C, bits)
         if rb < 0:
             _check(RPTQ_ERR_UNSUPPORTED, "rptq_kv_row_bytes")
-        out = torch.empty((T, rb), dtype=torch.uint8, device=kv.device)
+        out = _empty((T, rb), torch.uint8, kv.device, stream)
     st = lib().rptq_kv_quant_pack(_dp(kv), T, C, _dp(R), _hp(b), b.size - 1, _hp(sh), _hp(zh), bits,
                                   _dp(out), _stream(stream))
     _check(st, "rptq_kv_quant_pack")
@@ -288,10 +298,10 @@ def rptq_kv_attention(q, k_packed, v_packed, B, T, C, head_dim, scale, k_params,
     bk = _h(bk, np.int32); sk = _h(sk, np.float32); zk = _h(zk, np.int32)
     bv = _h(bv, np.int32); sv = _h(sv, np.float32); zv = _h(zv, np.int32)
     if out is None:
-        out = torch.empty((B, C), dtype=torch.float32, device=q.device)
+        out = _empty((B, C), torch.float32, q.device, stream)
     need = rptq_kv_attention_workspace_bytes(B, T, C, head_dim)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().rptq_kv_attention(_dp(q), _dp(k_packed), _dp(v_packed), B, T, C, head_dim, scale, _dp(Rk),
                                  _hp(bk), bk.size - 1, _hp(sk), _hp(zk), _dp(Rv), _hp(bv), bv.size - 1,
@@ -305,7 +315,7 @@ def rptq_kv_dequant(packed, C, R, bounds, s, z, bits, out=None, stream=None):
     T = packed.shape[0]
     b = _h(bounds, np.int32); sh = _h(s, np.float32); zh = _h(z, np.int32)
     if out is None:
-        out = torch.empty((T, C), dtype=torch.float16, device=packed.device)
+        out = _empty((T, C), torch.float16, packed.device, stream)
     st = lib().rptq_kv_dequant(_dp(packed), T, C, _dp(R), _hp(b), b.size - 1, _hp(sh), _hp(zh), bits,
                                _dp(out), _stream(stream))
     _check(st, "rptq_kv_dequant")
@@ -316,8 +326,8 @@ def rptq_kv_dequant(packed, C, R, bounds, s, z, bits, out=None, stream=None):
 def rptq_calib_minmax(x, mode=RPTQ_IN_FP16_RAW, gamma=None, beta=None, eps=1e-5, stream=None):
     """x: cuda fp16 [M][K].  Returns (mx, mn) cuda fp32 [K], natural order."""
     M, K = x.shape
-    mx = torch.empty(K, dtype=torch.float32, device=x.device)
-    mn = torch.empty(K, dtype=torch.float32, device=x.device)
+    mx = _empty(K, torch.float32, x.device, stream)
+    mn = _empty(K, torch.float32, x.device, stream)
     st = lib().rptq_calib_minmax(_dp(x), mode, M, K, _dp(gamma), _dp(beta), eps, _dp(mx), _dp(mn),
                                  _stream(stream))
     _check(st, "rptq_calib_minmax")

@@ -259,6 +259,7 @@ GEMM_CASES = [  # (M, K, N, g, a_bits, w_bits)
     (77, 512, 101, 4, 4, 4),            # odd N: a ragged last column tile
     (3, 768, 1, 2, 8, 8),               # N = 1
     (130, 40, 33, 2, 3, 3),             # K = 40 (two clusters padded to 64 codes), odd N
+    (1300, 512, 520, 4, 4, 4),          # 11 x 5 tiles: a partial last group of the grouped tile walk
 ]
 
 
