@@ -221,6 +221,30 @@ int rptq_ln_reorder_quant_dynamic(const void* x, int32_t in_mode, int64_t M, int
 int64_t rptq_ln_dynamic_workspace_bytes(int32_t g);
 
 /*
+ * rptq_ln_reorder_quant_dynamic without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing: the ranges pass's
+ * per-workgroup (lo, hi) partials go to a library-owned device array of
+ * RPTQ_LN_DYNAMIC_SCRATCH_BYTES (512 KB, room for RPTQ_MAX_CLUSTERS
+ * clusters), of which each GPU the library runs on holds its own copy until
+ * the process ends; its device address is looked up once per device, on the
+ * first call with that device current.  Every slot the quantizing launches
+ * read is written earlier in the same call, so nothing needs clearing, and a
+ * call leaves its partials behind.  All calls on one GPU share that GPU's
+ * array: calls that may overlap on one GPU (several streams, several host
+ * threads) race and must be serialized by the caller.
+ * Arguments, results, limits and errors are those of
+ * rptq_ln_reorder_quant_dynamic without workspace / workspace_bytes; a g
+ * whose partials would not fit the array is RPTQ_ERR_UNSUPPORTED (no legal
+ * g does), a failed address lookup RPTQ_ERR_HIP.
+ */
+#define RPTQ_LN_DYNAMIC_SCRATCH_BYTES (1024 * 2 * RPTQ_MAX_CLUSTERS * 4)
+int rptq_ln_reorder_quant_dynamic_noalloc(const void* x, int32_t in_mode, int64_t M, int32_t K,
+                                          const float* gamma_r, const float* beta_r, float eps,
+                                          const int32_t* R, const int32_t* bounds, int32_t g, int32_t bits,
+                                          uint8_t* codes, float* s_out, int32_t* z_out, void* stream);
+
+/*
  * rptq_qgemm with the activation clusters' (s, z) in DEVICE memory (s_dev
  * fp32 [g], z_dev int32 [g], e.g. the outputs of
  * rptq_ln_reorder_quant_dynamic), so no host round trip sits between the

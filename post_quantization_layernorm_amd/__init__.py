@@ -36,6 +36,7 @@ RPTQ_MAX_K = 16384
 
 EXPORTED = [
     "rptq_ln_reorder_quant", "rptq_ln_reorder_quant_dynamic", "rptq_ln_dynamic_workspace_bytes",
+    "rptq_ln_reorder_quant_dynamic_noalloc",
     "rptq_qgemm", "rptq_qgemm_dynamic",
     "rptq_qgemm_quant", "rptq_kv_quant_pack", "rptq_kv_dequant",
     "rptq_kv_attention", "rptq_kv_attention_workspace_bytes",
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "rptq_ln_reorder_quant_dynamic": (_I32, [_P, _I32, _I64, _I32, _P, _P, ctypes.c_float, _P, _P,
                                                      _I32, _I32, _P, _P, _P, _P, _I64, _P]),
             "rptq_ln_dynamic_workspace_bytes": (_I64, [_I32]),
+            "rptq_ln_reorder_quant_dynamic_noalloc": (_I32, [_P, _I32, _I64, _I32, _P, _P, ctypes.c_float, _P, _P,
+                                                             _I32, _I32, _P, _P, _P, _P]),
             "rptq_qgemm": (_I32, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
             "rptq_qgemm_dynamic": (_I32, [_P, _I64, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _P,
                                           _P]),
@@ -221,6 +224,21 @@ def rptq_ln_reorder_quant_dynamic(x, R, gamma_r, beta_r, bounds, bits, eps=1e-5,
                                              _hp(b), g, bits, _dp(out), _dp(s_out), _dp(z_out), _dp(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "rptq_ln_reorder_quant_dynamic")
+    return out, s_out, z_out
+
+
+def rptq_ln_reorder_quant_dynamic_noalloc(x, R, gamma_r, beta_r, bounds, bits, out, s_out, z_out, eps=1e-5,
+                                          in_mode=RPTQ_IN_FP16_RAW, stream=None):
+    """rptq_ln_reorder_quant_dynamic with the library's own partials array
+    instead of a workspace: the caller passes every output (codes cuda uint8
+    [M][row_bytes], s_out cuda fp32 [g], z_out cuda int32 [g]) and nothing is
+    allocated on the device.  Calls that may overlap on one GPU race."""
+    M, K = x.shape
+    b = _h(bounds, np.int32); g = b.size - 1
+    st = lib().rptq_ln_reorder_quant_dynamic_noalloc(_dp(x), in_mode, M, K, _dp(gamma_r), _dp(beta_r), eps,
+                                                     _dp(R), _hp(b), g, bits, _dp(out), _dp(s_out), _dp(z_out),
+                                                     _stream(stream))
+    _check(st, "rptq_ln_reorder_quant_dynamic_noalloc")
     return out, s_out, z_out
 
 

@@ -23,19 +23,29 @@
 //   - the row is parked in LDS in natural order; each unit gathers its 8
 //     inputs by R, normalizes, quantizes and packs them into an LDS copy of
 //     the output row, which is written with 16-byte stores.
+#include <mutex>
+
 #include "rptq_device.hpp"
 #include "../../include/rptq.h"
+
+// Partials of the dynamic-range ranges pass for callers that cannot allocate
+// (allocation-free entry point): one (lo, hi) pair per cluster for each of at
+// most kLnRangesMaxGrid workgroups, 512 KB.  Each GPU the library runs on
+// holds its own copy until the process ends.  Host code never uses this name
+// as an address: ln_dynamic_scratch() looks the device address up once per
+// device (hipGetSymbolAddress) and hands that out.
+static __device__ __align__(256) float scratch[rptq::kLnRangesMaxGrid * 2 * rptq::kMaxClusters];
 
 namespace rptq {
 namespace {
 
-__device__ __forceinline__ float block_sum(float v, float* scratch) {
+__device__ __forceinline__ float block_sum(float v, float* red) {
     v = wave_sum(v);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    if (lane == 0) scratch[w] = v;
+    if (lane == 0) red[w] = v;
     __syncthreads();
     float t = 0.0f;
-    for (int i = 0; i < nw; ++i) t += scratch[i];
+    for (int i = 0; i < nw; ++i) t += red[i];
     __syncthreads();
     return t;
 }
@@ -523,6 +533,31 @@ hipError_t launch_ln_reorder_quant_dynamic(const void* x, int in_mode, int64_t M
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_mode(kDevParams, x, in_mode, M, K, gamma_r, beta_r, eps, R, ca, row_bytes, codes, s_out,
                        z_out, 0, stream);
+}
+
+int64_t ln_dynamic_scratch_bytes() { return (int64_t)sizeof(scratch); }
+
+hipError_t ln_dynamic_scratch(void** ptr) {
+    // device address of this GPU's copy of the array, looked up on the first
+    // call with that device current and kept for the life of the process
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    *ptr = nullptr;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace rptq

@@ -195,11 +195,14 @@ int rptq_ln_reorder_quant(const void* x, int32_t in_mode, int64_t M, int32_t K,
                       "rptq_ln_reorder_quant launch");
 }
 
-int rptq_ln_reorder_quant_dynamic(const void* x, int32_t in_mode, int64_t M, int32_t K,
-                                  const float* gamma_r, const float* beta_r, float eps,
-                                  const int32_t* R, const int32_t* bounds, int32_t g, int32_t bits,
-                                  uint8_t* codes, float* s_out, int32_t* z_out, void* workspace,
-                                  int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// Shared by the two dynamic-range entry points: validation, the cluster
+// table, the three launches with the partials in `partials`.
+static int ln_dynamic_common(const void* x, int32_t in_mode, int64_t M, int32_t K, const float* gamma_r,
+                             const float* beta_r, float eps, const int32_t* R, const int32_t* bounds, int32_t g,
+                             int32_t bits, uint8_t* codes, float* s_out, int32_t* z_out, void* workspace,
+                             int64_t workspace_bytes, bool own_scratch, void* stream, const char* what) {
     if (in_mode != RPTQ_IN_FP16_RAW && in_mode != RPTQ_IN_FP32_NORMALIZED)
         return fail(RPTQ_ERR_INVALID_ARG, "in_mode = %d", in_mode);
     if (M < 1) return fail(RPTQ_ERR_INVALID_ARG, "M = %lld < 1: dynamic ranges need rows", (long long)M);
@@ -213,14 +216,25 @@ int rptq_ln_reorder_quant_dynamic(const void* x, int32_t in_mode, int64_t M, int
     }
     if (K % 8) return fail(RPTQ_ERR_UNSUPPORTED, "K = %d is not a multiple of 8", K);
     if (K > kMaxK) return fail(RPTQ_ERR_UNSUPPORTED, "K = %d exceeds %d", K, kMaxK);
-    if (!x || !codes || !s_out || !z_out || !workspace)
+    if (!x || !codes || !s_out || !z_out || (!own_scratch && !workspace))
         return fail(RPTQ_ERR_INVALID_ARG, "x, codes, s_out, z_out or workspace is NULL");
-    if (workspace_bytes < rptq_ln_dynamic_workspace_bytes(g))
+    const int64_t need = rptq_ln_dynamic_workspace_bytes(g);
+    if (own_scratch) {
+        if (need > ln_dynamic_scratch_bytes())
+            return fail(RPTQ_ERR_UNSUPPORTED, "g = %d needs %lld bytes of partials, more than the library's "
+                        "%lld-byte array", g, (long long)need, (long long)ln_dynamic_scratch_bytes());
+    } else if (workspace_bytes < need) {
         return fail(RPTQ_ERR_INVALID_ARG, "workspace_bytes = %lld < %lld", (long long)workspace_bytes,
-                    (long long)rptq_ln_dynamic_workspace_bytes(g));
-    if (!aligned16(x) || !aligned16(codes) || !aligned16(s_out) || !aligned16(z_out) || !aligned16(workspace) ||
+                    (long long)need);
+    }
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(s_out) || !aligned16(z_out) ||
+        (!own_scratch && !aligned16(workspace)) ||
         (in_mode == RPTQ_IN_FP16_RAW && (!aligned16(gamma_r) || !aligned16(beta_r) || (R && !aligned16(R)))))
         return fail(RPTQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    if (own_scratch) {
+        const hipError_t e = ln_dynamic_scratch(&workspace);
+        if (e != hipSuccess) return hip_status(e, "device address of the library's partials array");
+    }
     // the cluster table's own (s, z) are unused: placeholders
     float s1[kMaxClusters];
     int32_t z0[kMaxClusters];
@@ -231,7 +245,26 @@ int rptq_ln_reorder_quant_dynamic(const void* x, int32_t in_mode, int64_t M, int
                                                       in_mode == RPTQ_IN_FP16_RAW ? R : nullptr, ca, row_bytes,
                                                       codes, s_out, z_out, static_cast<float*>(workspace),
                                                       (hipStream_t)stream),
-                      "rptq_ln_reorder_quant_dynamic launch");
+                      what);
+}
+
+extern "C" {
+
+int rptq_ln_reorder_quant_dynamic(const void* x, int32_t in_mode, int64_t M, int32_t K,
+                                  const float* gamma_r, const float* beta_r, float eps,
+                                  const int32_t* R, const int32_t* bounds, int32_t g, int32_t bits,
+                                  uint8_t* codes, float* s_out, int32_t* z_out, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+    return ln_dynamic_common(x, in_mode, M, K, gamma_r, beta_r, eps, R, bounds, g, bits, codes, s_out, z_out,
+                             workspace, workspace_bytes, false, stream, "rptq_ln_reorder_quant_dynamic launch");
+}
+
+int rptq_ln_reorder_quant_dynamic_noalloc(const void* x, int32_t in_mode, int64_t M, int32_t K,
+                                          const float* gamma_r, const float* beta_r, float eps,
+                                          const int32_t* R, const int32_t* bounds, int32_t g, int32_t bits,
+                                          uint8_t* codes, float* s_out, int32_t* z_out, void* stream) {
+    return ln_dynamic_common(x, in_mode, M, K, gamma_r, beta_r, eps, R, bounds, g, bits, codes, s_out, z_out,
+                             nullptr, 0, true, stream, "rptq_ln_reorder_quant_dynamic_noalloc launch");
 }
 
 int64_t rptq_ln_dynamic_workspace_bytes(int32_t g) {

@@ -78,6 +78,12 @@ hipError_t launch_ln_reorder_quant_dynamic(const void* x, int in_mode, int64_t M
                                            uint8_t* codes, float* s_out, int32_t* z_out, float* partials,
                                            hipStream_t stream);
 
+// Allocation-free dynamic ranges: the partials live in a library-owned
+// device array (one per GPU) instead of a caller workspace.  Its size, and
+// its device address on the current device (looked up on first use).
+int64_t ln_dynamic_scratch_bytes();
+hipError_t ln_dynamic_scratch(void** ptr);
+
 hipError_t launch_kv_quant_pack(const uint16_t* kv, int64_t T, int32_t C, const int32_t* R,
                                 const ClusterArgs& ca, uint8_t* packed, hipStream_t stream);
 

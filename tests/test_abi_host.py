@@ -401,3 +401,27 @@ def test_abi_from_plain_c(P, tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert r.stdout.split()[-1] == "0"
+
+
+def _ln_dyn_noalloc(P, **kw):
+    a = dict(x=FAKE, mode=0, M=8, K=64, gamma=FAKE, beta=FAKE, eps=1e-5, R=None,
+             bounds=np.array([0, 16, 64], np.int32), bits=4, codes=FAKE, s=FAKE, z=FAKE)
+    a.update(kw)
+    return P.lib().rptq_ln_reorder_quant_dynamic_noalloc(a["x"], a["mode"], a["M"], a["K"], a["gamma"], a["beta"],
+                                                         a["eps"], a["R"], _vp(a["bounds"]), a["bounds"].size - 1,
+                                                         a["bits"], a["codes"], a["s"], a["z"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=5), -1), (dict(mode=7), -1), (dict(M=0), -1), (dict(M=-1), -1), (dict(K=0), -1),
+    (dict(bounds=np.array([0, 16, 60], np.int32)), -1), (dict(bounds=np.array([0, 16, 16, 64], np.int32)), -1),
+    (dict(eps=0.0), -1), (dict(gamma=None), -1), (dict(x=None), -1), (dict(codes=None), -1),
+    (dict(s=None), -1), (dict(z=None), -1),
+    (dict(K=60, bounds=np.array([0, 16, 60], np.int32)), -2),
+    (dict(x=MISALIGNED), -3), (dict(s=MISALIGNED), -3), (dict(z=MISALIGNED), -3),
+])
+def test_ln_reorder_quant_dynamic_noalloc_rejects(P, kw, status):
+    """The allocation-free variant validates like the workspace one (minus
+    the workspace) before any HIP call."""
+    assert _ln_dyn_noalloc(P, **kw) == status
+    assert P.lib().rptq_last_error().decode()
