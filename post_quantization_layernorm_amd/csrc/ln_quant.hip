@@ -235,6 +235,24 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
                 }
             }
     }
+    // LayerNorm mode, quantizing passes: gamma' and beta' carry the unit's
+    // 1/s, so fma(gamma'/s, n, beta'/s) is y/s (one more rounding than
+    // forming y first, well inside the code tolerance of the fused path) and
+    // the code is its sum with 1.5 * 2^23 + z (rounded to an integer, ties to
+    // even) clamped: one op less per element.  (Quant-only mode keeps the
+    // single rounding of y * (1/s).)
+    [[maybe_unused]] float umz[UPL];
+    if constexpr (LN && DM != kRanges) {
+#pragma unroll
+        for (int u = 0; u < UPL; ++u) {
+            umz[u] = kRoundMagic + uzf[u];            // exact: |z| <= 2^21
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                gam[u][e] *= uinv[u];
+                bet[u][e] *= uinv[u];
+            }
+        }
+    }
     // units holding at least one real position (bit u)
     uint32_t ureal = 0;
 #pragma unroll
@@ -347,7 +365,14 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
             for (int u = 0; u < UPL; ++u) {
                 uint32_t qb[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qb[e] = quant_bits(y_of(u, e), uinv[u], uzf[u], qhi);
+                for (int e = 0; e < 8; ++e) {
+                    if constexpr (LN) {
+                        const float t = y_of(u, e) + umz[u];      // y_of gives y / s here
+                        qb[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(t, kRoundMagic, qhi));
+                    } else {
+                        qb[e] = quant_bits(y_of(u, e), uinv[u], uzf[u], qhi);
+                    }
+                }
                 store_unit_bits<BITS>(orow + uob[u], qb);
             }
         }

@@ -10,6 +10,7 @@ namespace rptq {
 constexpr int kMaxClusters = 64;
 constexpr int kMaxK = 16384;
 constexpr int kMaxBlock = 512;         // largest workgroup of the streaming kernels
+constexpr int kKvPackMaxBlock = 1024;  // K/V pack: one wide workgroup per compute unit
 constexpr int kMaxUpl = 5;             // most units (8 codes each) one lane handles
 #ifndef RPTQ_LN_MAX_BLOCK
 #define RPTQ_LN_MAX_BLOCK 256          // LayerNorm kernel: fewer, fatter lanes (two workgroups per CU)

@@ -281,6 +281,29 @@ def test_qgemm_accumulators_bit_exact_and_y(P, case):
     assert torch.equal(Y, Y2)
 
 
+# More than 256 tiles (several workgroups per compute unit, both grouped
+# tile walks of every XCD complete): every accumulator and Y against the
+# oracle, for 4-, 8- and 3-bit codes.
+@pytest.mark.parametrize("case", [(2048, 1024, 2176, 8, 4, 4), (1024, 768, 4224, 4, 8, 8),
+                                  (1536, 1280, 2816, 16, 3, 3)],
+                         ids=lambda c: "M{}K{}N{}g{}A{}W{}".format(*c))
+def test_qgemm_many_tiles_bit_exact(P, case):
+    M, K, N, g, ab, wb = case
+    _say("gemm many tiles", case)
+    c = layer_case(M, K, N, g, ab, wb, seed=M + N)
+    q, codes = _oracle_codes(c)
+    Y_o, acc_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w, return_acc=True)
+    wp, cs, sw = _gemm_inputs(P, c)
+    acc = torch.full((g, M, N), -7, dtype=torch.int32, device="cuda")
+    Y = P.rptq_qgemm(dev(codes), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs, acc_debug=acc)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_o)
+    del acc
+    assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
+    Y2 = P.rptq_qgemm(dev(codes), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs)
+    assert torch.equal(Y, Y2)
+
+
 @pytest.mark.parametrize("bounds", [[0, 1, 2, 3, 64, 96, 97, 160, 256], [0, 256],
                                     list(range(0, 65)) + [256]],
                          ids=["size1", "g1", "g65"])
