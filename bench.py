@@ -15,6 +15,14 @@ stream the kernels are launched on; the other kernels' rates are extra keys.
 `--gpus N` with N > 1 is refused: the library drives one GPU per process and
 has no multi-GPU path.
 
+Each timed step is preceded by a 1 GiB device write that flushes L2 and the
+MALL (outside the kernel events); per-kernel times are medians over the
+timed steps, with p10 / p90 and the mean beside them.  After the timed steps,
+the three smaller layers (OPT-125m W8A8, OPT-1.3B fc1 W4A4, OPT-13B QKV W4A4
+and W4A8) are timed cold and cache-resident (their inputs fit the MALL), and
+the CPU baseline (the oracle) runs a row sample of the W4A4 layer and one
+8192-token batch of the K/V pack.
+
 Profiling helpers (not part of the timed step):
   --copy-probe       after the timed region, one plain device copy of
                      COPY_PROBE_BYTES, whose counter readings calibrate the HBM
@@ -22,7 +30,9 @@ Profiling helpers (not part of the timed step):
   --ingest-pmc F W   read two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then
                      WRITE_SIZE), scale them by the copy probe and write the
                      per-launch HBM traffic of each kernel to
-                     profiles/hbm_traffic.json.
+                     profiles/hbm_traffic.json;
+  --summarize-pmc CSV...  per-dispatch counters with derived rates (MFMA busy,
+                     clock, LDS activity).
 """
 from __future__ import annotations
 
@@ -85,6 +95,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline leg (0: leave it out)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="leave out the cache flush (a 1 GiB device write) before each timed step")
+    ap.add_argument("--no-small-configs", action="store_true",
+                    help="leave out the OPT-125m / OPT-1.3B / OPT-13B layer timings after the timed steps")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed region, run one plain device copy of COPY_PROBE_BYTES")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -264,9 +278,14 @@ def main():
 
     nev = len(names) + 1
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    # L2 + MALL flush before every step (outside the kernel events; inside
+    # the wall-clock of the steps, ~0.2 ms of a ~50 ms step)
+    flush_buf = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0xFF)
         step(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -274,8 +293,13 @@ def main():
     for ev in events:
         for j, n in enumerate(names):
             per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)      # seconds
-    avg = {n: float(np.mean(v)) for n, v in per.items()}
-    log("[bench] per-kernel avg ms: " + ", ".join(f"{n}={avg[n] * 1e3:.3f}" for n in names))
+    # per-kernel medians (robust to one slow launch); mean and p10 / p90 are
+    # reported beside them
+    avg = {n: float(np.median(v)) for n, v in per.items()}
+    stats = {n: {"median": float(np.median(v)) * 1e3, "mean": float(np.mean(v)) * 1e3,
+                 "p10": float(np.percentile(v, 10)) * 1e3, "p90": float(np.percentile(v, 90)) * 1e3}
+             for n, v in per.items()}
+    log("[bench] per-kernel median ms: " + ", ".join(f"{n}={avg[n] * 1e3:.3f}" for n in names))
 
     ops = 2.0 * M * N * K
     res_layer = {}
@@ -320,6 +344,13 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, x, gamma, beta, R, bounds, variants[4]["s"], variants[4]["z"], N, args.cpu_seconds)
+        cpu["kv"] = cpu_baseline_kv({n: (kv[n]["x"], kv[n]["R"].cpu().numpy(), kv[n]["bounds"], kv[n]["s"],
+                                         kv[n]["z"]) for n in ("K", "V")}, C, kvb)
+    small = None
+    if not args.no_small_configs:
+        del Y, wts, variants, qout, dyn, kv
+        torch.cuda.empty_cache()
+        small = small_configs(P, torch, dev, stream, flush_buf)
 
     line = {
         "metric": "tokens/s + TOPS of fused LN-quant->qGEMM (% int8 MFMA peak); KV-pack GB/s",
@@ -360,9 +391,15 @@ def main():
                  "tokens_per_s": M / (avg["ln3"] + avg["gemm3w3"])},
         **out,
         "per_kernel_ms": {n: avg[n] * 1e3 for n in names},
+        "per_kernel_ms_stats": stats,
+        "timing": ("HIP events on the launch stream around each kernel, median over the timed steps "
+                   "(p10 / p90 and mean in per_kernel_ms_stats); " +
+                   ("a 1 GiB device write flushes L2 and the MALL before every step"
+                    if flush_buf is not None else "no cache flush")),
         "roofline": roofline,
         "rooflines": rooflines,
         "cpu_baseline": cpu,
+        "smaller_layers": small,
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
@@ -443,7 +480,77 @@ def ingest_pmc(fetch_csv, write_csv, out_path=None):
     return res
 
 
+FLUSH_BYTES = 1 << 30                   # > 8 x 4 MB L2 + 256 MB MALL
 N_XCD, N_CU, N_SIMD = 8, 256, 1024      # MI355X
+
+
+def _time_launches(torch, stream, fn, iters, flush_buf=None):
+    """HIP-event times (seconds) of `iters` launches of fn on `stream`; with
+    flush_buf, a cache flush before each launch (outside the events)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * iters)]
+    for i in range(iters):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0xFF)
+        ev[2 * i].record(stream)
+        fn()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e-3 for i in range(iters)])
+
+
+def small_configs(P, torch, dev, stream, flush_buf, iters=20):
+    """The OPT-125m (W8A8), OPT-1.3B fc1 (W4A4) and OPT-13B QKV (W4A4, W4A8)
+    layers: fused LayerNorm-quant and segmented GEMM, each timed cold (cache
+    flushed before every launch) and warm (launches back to back, inputs
+    resident in the 256 MB MALL / L2).  Their LayerNorm inputs (0.2-42 MB)
+    fit the MALL, so their HBM fractions are cache-assisted, not HBM rates."""
+    import synthetic
+    res = {}
+    for name, ab in (("opt125m_w8a8", 8), ("opt1.3b_fc1_w4a4", 4), ("opt13b_qkv_w4a4", 4), ("opt13b_qkv_w4a4", 8)):
+        w = synthetic.WORKLOADS[name]
+        M, K, N, g, wb = w.M, w.K, w.N, w.g, w.w_bits
+        mu, sg = synthetic.channel_params(K, w.seed, w.outlier_frac, range_ratio=w.range_ratio)
+        gamma, beta = synthetic.ln_params(K, w.seed, random=False)
+        g_d = torch.from_numpy(gamma).to(dev); b_d = torch.from_numpy(beta).to(dev)
+        xc = torch.from_numpy(synthetic.tokens(w.calib_tokens, mu, sg, w.seed, synthetic.STREAM_CALIB)).to(dev)
+        mx, mn = P.rptq_calib_minmax(xc, P.RPTQ_IN_FP16_RAW, g_d, b_d)
+        mx, mn = mx.cpu().numpy(), mn.cpu().numpy()
+        R, bounds = P.rptq_kmeans_reorder(mx, mn, g, synthetic.kmeans_uniforms(w.seed, 10, g), n_init=10)
+        s, z = P.rptq_cluster_params(mx, mn, R, bounds, ab)
+        R_d = torch.from_numpy(R).to(dev)
+        gr, br = g_d[R_d].contiguous(), b_d[R_d].contiguous()
+        x = torch.from_numpy(synthetic.tokens(M, mu, sg, w.seed, synthetic.STREAM_EVAL)).to(dev)
+        wq, s_w = P.rptq_quantize_weights(synthetic.weights(K, N, w.seed), wb)
+        wp, cs = P.rptq_pack_weights(wq, R, bounds, wb)
+        wp, cs, sw = (torch.from_numpy(a).to(dev) for a in (wp, cs, s_w))
+        codes = torch.empty((M, P.rptq_codes_row_bytes(bounds, ab)), dtype=torch.uint8, device=dev)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ln = lambda: P.rptq_ln_reorder_quant(x, R_d, gr, br, bounds, s, z, ab, out=codes, stream=stream)
+        gm = lambda: P.rptq_qgemm(codes, M, K, N, bounds, s, z, ab, wp, wb, sw, cs, out=Y, stream=stream)
+        for _ in range(3):
+            ln(); gm()
+        torch.cuda.synchronize()
+        ops, ln_bytes = 2.0 * M * N * K, M * K * (2 + ab / 8)
+        entry = {"M": M, "K": K, "N": N, "g": g, "a_bits": ab, "w_bits": wb, "K_pad": P.rptq_codes_kpad(bounds)}
+        for mode, fb in (("cold", flush_buf), ("warm_cache_resident", None)):
+            t_ln = _time_launches(torch, stream, ln, iters, fb)
+            t_gm = _time_launches(torch, stream, gm, iters, fb)
+            mln, mgm = float(np.median(t_ln)), float(np.median(t_gm))
+            entry[mode] = {
+                "ln_ms": {"median": mln * 1e3, "p10": float(np.percentile(t_ln, 10)) * 1e3,
+                          "p90": float(np.percentile(t_ln, 90)) * 1e3},
+                "gemm_ms": {"median": mgm * 1e3, "p10": float(np.percentile(t_gm, 10)) * 1e3,
+                            "p90": float(np.percentile(t_gm, 90)) * 1e3},
+                "tokens_per_s": M / (mln + mgm),
+                "gemm_tops": ops / mgm / 1e12, "gemm_frac_int8_peak": ops / mgm / 1e12 / INT8_PEAK_TOPS,
+                "ln_GBps": ln_bytes / mln / 1e9, "ln_frac_hbm_peak": ln_bytes / mln / 1e9 / HBM_PEAK_GBPS}
+        res[f"{name}_a{ab}"] = entry
+        log(f"[bench] {name} A{ab}: cold LN {entry['cold']['ln_ms']['median']:.4f} ms, GEMM "
+            f"{entry['cold']['gemm_ms']['median']:.4f} ms ({entry['cold']['gemm_tops']:.0f} TOPS); warm LN "
+            f"{entry['warm_cache_resident']['ln_ms']['median']:.4f} ms, GEMM "
+            f"{entry['warm_cache_resident']['gemm_ms']['median']:.4f} ms")
+        del x, codes, Y, wp, cs, sw
+    return res
 
 
 def summarize_pmc(paths):
@@ -510,6 +617,23 @@ def cpu_baseline(w, x_dev, gamma, beta, R, bounds, s, z, N, budget_s):
         done += chunk
     return {"value": done / t_tot, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
             "sample": f"{done} of {w.M} tokens of the W4A4 layer (LN+quant+pack+segmented GEMM, N={N})",
+            "seconds": t_tot}
+
+
+def cpu_baseline_kv(tensors, C, bits, rows=8192):
+    """The oracle's K/V quantize + pack on one 8192-token batch of K and of V
+    (the first batch of each cache), in GB/s of the same algorithmic bytes
+    as the GPU kernel (fp16 in + packed codes out)."""
+    import oracle as orc
+    t_tot, nbytes = 0.0, 0
+    for name, (x_dev, R, bounds, s, z) in tensors.items():
+        xs = x_dev[:rows].cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        orc.kv_quant_pack(xs, R, bounds, s, z, bits)
+        t_tot += time.perf_counter() - t0
+        nbytes += rows * C * (2 + bits / 8)
+    return {"value": nbytes / t_tot / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"K/V quantize + pack, one {rows}-token batch of K and of V ({C} channels, {bits} bit)",
             "seconds": t_tot}
 
 
