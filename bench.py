@@ -484,10 +484,33 @@ FLUSH_BYTES = 1 << 30                   # > 8 x 4 MB L2 + 256 MB MALL
 N_XCD, N_CU, N_SIMD = 8, 256, 1024      # MI355X
 
 
+_SLEEP_CYCLES_PER_MS = []
+
+
+def _gpu_sleep_ms(torch, stream, ms):
+    """Keep `stream` busy for about `ms` milliseconds with a spin kernel that
+    touches no memory (calibrated once against HIP events)."""
+    if not _SLEEP_CYCLES_PER_MS:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.cuda._sleep(1 << 22)
+        e1.record(stream)
+        e1.synchronize()
+        _SLEEP_CYCLES_PER_MS.append((1 << 22) / max(e0.elapsed_time(e1), 1e-3))
+    torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS[0]))
+
+
 def _time_launches(torch, stream, fn, iters, flush_buf=None):
     """HIP-event times (seconds) of `iters` launches of fn on `stream`; with
-    flush_buf, a cache flush before each launch (outside the events)."""
+    flush_buf, a cache flush before each launch (outside the events).
+    Without it the launches run back to back on warm caches: a spin kernel
+    holds the stream while they are queued, so no launch waits for the host
+    (short kernels would otherwise be timed together with the host's
+    enqueue latency)."""
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * iters)]
+    if flush_buf is None:
+        fn()
+        _gpu_sleep_ms(torch, stream, 2.0 + 0.2 * iters)
     for i in range(iters):
         if flush_buf is not None:
             flush_buf.fill_(i & 0xFF)
@@ -573,7 +596,9 @@ def summarize_pmc(paths):
             d["c"][r["Counter_Name"]] += float(r["Counter_Value"])
         for (disp, name, grid), d in per.items():
             c = d["c"]
-            out = {"file": os.path.basename(path), "dispatch": disp, "kernel": name.split("(")[0],
+            short = name.replace("(anonymous namespace)::", "")
+            short = short[5:] if short.startswith("void ") else short
+            out = {"file": os.path.basename(path), "dispatch": disp, "kernel": short.split("(")[0],
                    "grid_threads": grid, "dur_us": d["dur_ns"] / 1e3, "counters": dict(c)}
             if "GRBM_GUI_ACTIVE" in c:
                 cyc = c["GRBM_GUI_ACTIVE"] / N_XCD
@@ -589,6 +614,26 @@ def summarize_pmc(paths):
                 out["mfma_int8_ops"] = c["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512
             if "SQ_ACTIVE_INST_VALU" in c and "SQ_WAVE_CYCLES" in c and c["SQ_WAVE_CYCLES"]:
                 out["valu_active_frac_of_wave_cycles"] = c["SQ_ACTIVE_INST_VALU"] / c["SQ_WAVE_CYCLES"]
+            if "GRBM_GUI_ACTIVE" in c:
+                simd_cyc = N_SIMD * c["GRBM_GUI_ACTIVE"] / N_XCD
+                # SQ_ACTIVE_INST_VALU counts 4-cycle issue slots of a wave64 VALU instruction
+                if "SQ_ACTIVE_INST_VALU" in c:
+                    out["valu_busy_frac"] = 4 * c["SQ_ACTIVE_INST_VALU"] / simd_cyc
+                if "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
+                    out["valu_mfma_coexec_frac"] = c["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cyc
+                if "TA_TA_BUSY" in c:
+                    out["ta_busy_frac"] = c["TA_TA_BUSY"] / (N_CU * c["GRBM_GUI_ACTIVE"] / N_XCD)
+            if c.get("SQ_WAVE_CYCLES"):
+                for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY"):
+                    if k in c:
+                        out[k.lower()[3:] + "_frac_of_wave_cycles"] = c[k] / c["SQ_WAVE_CYCLES"]
+            waves = grid / 64
+            for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU"):
+                if k in c:
+                    out[k.lower()[3:] + "_per_wave"] = c[k] / waves
+            if c.get("SQ_INSTS_VMEM_RD") and "SQ_INST_LEVEL_VMEM" in c:
+                # in-flight level accumulated per cycle over instructions issued: mean residence
+                out["vmem_level_per_vmem_rd"] = c["SQ_INST_LEVEL_VMEM"] / c["SQ_INSTS_VMEM_RD"]
             rows.append(out)
             print(json.dumps(out))
     return rows
