@@ -229,15 +229,21 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     // Pieces of steps past the end of K read as zero (offset beyond the
     // buffer), so the MFMAs of a partial last stage add nothing.
     using Stage = StageRegs<ABITS, WBITS, PA, PB>;
-    auto gload = [&](Stage& S, int st) {
-        const int64_t ao = (int64_t)st * (SK * APIECE), bo = (int64_t)st * (SK * BPIECE);
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile + ao, a_left - ao);
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile + bo, b_left - bo);
+    // piece k (A pieces first, then W' pieces) of stage st into register set S
+    auto gload_piece = [&](Stage& S, int st, int k) {
         const int room = nsteps - st * SK;
+        if (k < PA) {
+            const int64_t ao = (int64_t)st * (SK * APIECE);
+            load_piece<ABITS>(make_rsrc(a_tile + ao, a_left - ao), a_step[k] < room ? a_voff[k] : 0x80000000u, S.a[k]);
+        } else {
+            const int64_t bo = (int64_t)st * (SK * BPIECE);
+            load_piece<WBITS>(make_rsrc(b_tile + bo, b_left - bo), b_step[k - PA] < room ? b_voff[k - PA] : 0x80000000u,
+                              S.b[k - PA]);
+        }
+    };
+    auto gload = [&](Stage& S, int st) {
 #pragma unroll
-        for (int i = 0; i < PA; ++i) load_piece<ABITS>(ra, a_step[i] < room ? a_voff[i] : 0x80000000u, S.a[i]);
-#pragma unroll
-        for (int i = 0; i < PB; ++i) load_piece<WBITS>(rb, b_step[i] < room ? b_voff[i] : 0x80000000u, S.b[i]);
+        for (int k = 0; k < NPIECE; ++k) gload_piece(S, st, k);
     };
     // stage piece k of register set S into LDS buffer buf
     auto put = [&](const Stage& S, int buf, int k) {
@@ -336,8 +342,9 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     // One stage: SK MFMA steps from LDS buffer `buf`; the fragments of step
     // ks + 1 are read before the MFMAs of step ks, and piece ks of the next
     // stage's staging registers `nxt` is unpacked into the other buffer in
-    // the same instruction stream (on the last stage that buffer is never
-    // read again, so the stores are harmless).
+    // the same instruction stream and reloaded (on the last stage that buffer
+    // is never read again, so the stores are harmless, and the reloads read
+    // zero pieces past the end of K).
     auto compute = [&](int buf, int st, Stage& nxt) {
         auto rd = [&](int slot, int ks) {
 #pragma unroll
@@ -365,8 +372,10 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
             const int cur = ks & 1;
             if (ks + 1 < SK) rd(cur ^ 1, ks + 1);
             if (ks + 1 < SK || last) mfmas(cur);
-            if (ks < NPIECE) put(nxt, buf ^ 1, ks);    // unused on the last stage
-            if (ks == NPIECE - 1) gload(nxt, st + 3);   // the set is free again: two stages ahead
+            if (ks < NPIECE) {
+                put(nxt, buf ^ 1, ks);                  // unused on the last stage
+                gload_piece(nxt, st + 3, ks);           // that piece is free again: reload it two stages ahead
+            }
             // issue order inside the step: each MFMA is followed by part of
             // the next step's fragment reads, the unpack VALU work, and last
             // the staging stores (so the reads never wait behind them)
@@ -386,9 +395,11 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     };
 
     // ---- pipeline: during stage st, register set R[(st + 1) & 1] holds
-    // stage st + 1, which is unpacked into the other LDS buffer and then
-    // reloaded with stage st + 3; R[st & 1] has stage st + 2 in flight.  Every
-    // load thus has about two stages to arrive.  One barrier per stage.
+    // stage st + 1, which is unpacked into the other LDS buffer piece by
+    // piece, each piece reloaded with stage st + 3 right after its unpack (one
+    // load per MFMA step rather than a burst); R[st & 1] has stage st + 2 in
+    // flight.  Every load thus has about two stages to arrive.  One barrier
+    // per stage.
     Stage R0, R1;
     gload(R0, 0);
     gload(R1, 1);
