@@ -5,17 +5,23 @@
 // sequence length they hold most of the memory.  Attention then has to read
 // them back; instead of a separate dequantize pass that writes the fp16
 // cache to HBM and an attention pass that reads it again, every packed row
-// is dequantized on its way into LDS (exactly as the standalone dequantize
-// computes it: fp16_rne(s_c * (q - z_c)), scattered back to natural channel
-// order) and consumed there.
+// is decoded on its way into LDS and consumed there.  The decode writes
+// each code's exact (q - z_c) as an fp16 integer, scattered back to natural
+// channel order (1024 + q is formed from the code bits, and one packed fp16
+// add of -(1024 + z_c) per pair of codes leaves q - z_c exactly); the
+// cluster scale s_c is applied in fp32 outside the per-row work: folded into
+// the query for the scores (q_c * s_c), and into each output channel of the
+// value sums at the end.  So the cache values enter the arithmetic as
+// s_c (q - z_c) without the fp16 rounding of the standalone dequantize (a
+// difference of at most half an fp16 ulp per value).
 //
 // One query token per sequence (decode).  Work is split flash-decoding
 // style: workgroup (b, k) handles tokens [k*TC, k*TC + TC) of sequence b in
 // three phases, the packed rows streaming through a ring of LDS slots
 // several rows ahead:
 //   1. scores: for each key row, LPH = D/16 lanes per head each take 16
-//      channels (packed-fp16 dot products), reduced with lane shuffles:
-//      S[t][h] = scale * q_h . k_h;
+//      channels (fp32 q_c * s_c against the fp16 (q - z_c)), reduced with
+//      lane shuffles: S[t][h] = scale * q_h . k_h;
 //   2. softmax inside the chunk: m_h = max_t S, p = exp(S - m_h), l_h = sum p;
 //   3. values: every lane owns 8-channel slices of the output and adds
 //      p[t][h] * v over the chunk's value rows.
@@ -37,11 +43,12 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Per code of the packed row (unit-major: code e of unit u at u * 8 + e):
-// its natural channel, and its cluster's s and z.
+// its natural channel and its cluster's z; and per natural channel, its
+// cluster's s.
 struct AttnTable {
     uint16_t* dst;
-    float* s;
-    float* z;
+    float* s;          // natural channel order
+    float* z;          // code order
 };
 
 template <int BITS>
@@ -52,8 +59,9 @@ __global__ __launch_bounds__(256) void kv_attn_tables_kernel(int32_t C, const in
     const int unit = i >> 3, e = i & 7;
     const int j = UnitGeom<BITS>::first(unit) + e * UnitGeom<BITS>::stride;
     const int c = cluster_of_pos(ca, j);
-    tb.dst[i] = (uint16_t)(R ? R[j] : j);
-    tb.s[i] = ca.s[c];
+    const int nat = R ? R[j] : j;
+    tb.dst[i] = (uint16_t)nat;
+    tb.s[nat] = ca.s[c];
     tb.z[i] = (float)ca.z[c];
 }
 
@@ -78,10 +86,11 @@ __global__ __launch_bounds__(kAttnBlock) void kv_attn_chunk_kernel(
     float* S = reinterpret_cast<float*>(dummy + 16);          // [TC][H]
     const int n_units = C / 8;
 
-    // per-lane units of 8 codes: destination byte in xrow, s and z of each
-    // code, read from the tables kv_attn_tables_kernel built once per call
+    // per-lane units of 8 codes: destination byte in xrow of each code, and
+    // per pair of codes the fp16 pair -(1024 + z) that turns 1024 + q into
+    // q - z, from the tables kv_attn_tables_kernel built once per call
     int dst[UPL][8], uib[UPL];
-    float sc[UPL][8], zf[UPL][8];
+    half2_t nz[UPL][4];
     auto tables = [&](const AttnTable& tb) {
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
@@ -91,18 +100,15 @@ __global__ __launch_bounds__(kAttnBlock) void kv_attn_chunk_kernel(
             const int uu = live ? unit : 0;
             const u32x4 d4 = *reinterpret_cast<const u32x4*>(tb.dst + uu * 8);
             const uint32_t dw[4] = {d4.x, d4.y, d4.z, d4.w};
-            const float4 s0 = reinterpret_cast<const float4*>(tb.s + uu * 8)[0];
-            const float4 s1 = reinterpret_cast<const float4*>(tb.s + uu * 8)[1];
             const float4 z0 = reinterpret_cast<const float4*>(tb.z + uu * 8)[0];
             const float4 z1 = reinterpret_cast<const float4*>(tb.z + uu * 8)[1];
-            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
             const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < 8; ++e)
                 dst[u][e] = live ? (int)((dw[e / 2] >> (16 * (e & 1))) & 0xFFFFu) * 2 : (int)(dummy - xrow);
-                sc[u][e] = sv[e];
-                zf[u][e] = zv[e];
-            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)       // integers up to 1279: exact in fp16
+                nz[u][i] = half2_t{(_Float16)(-1024.0f - zv[2 * i]), (_Float16)(-1024.0f - zv[2 * i + 1])};
         }
     };
 
@@ -171,8 +177,13 @@ __global__ __launch_bounds__(kAttnBlock) void kv_attn_chunk_kernel(
                     qv[7] = (b1 >> 6) | ((b2 >> 7) & 1) << 2;
                 }
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    *reinterpret_cast<_Float16*>(xrow + dst[u][e]) = (_Float16)(sc[u][e] * ((float)qv[e] - zf[u][e]));
+                for (int i = 0; i < 4; ++i) {
+                    // (1024 + q) pair from the code bits, + (-(1024 + z)) pair: q - z exactly
+                    const uint32_t w = (uint32_t)qv[2 * i] | (uint32_t)qv[2 * i + 1] << 16 | 0x64006400u;
+                    const uint32_t x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, w) + nz[u][i]);
+                    *reinterpret_cast<uint16_t*>(xrow + dst[u][2 * i]) = (uint16_t)x;
+                    *reinterpret_cast<uint16_t*>(xrow + dst[u][2 * i + 1]) = (uint16_t)(x >> 16);
+                }
             }
             lds_barrier();                                    // xrow holds row t; slot t free
             issue_row(rows, t + kAttnRing);
@@ -187,14 +198,28 @@ __global__ __launch_bounds__(kAttnBlock) void kv_attn_chunk_kernel(
     // consecutive, so the reduction is a few lane swaps.
     const int ntask = H * LPH;
     const int rounds = (ntask + kAttnBlock - 1) / kAttnBlock;
-    u32x4 qa[kAttnMaxRounds][2];
+    // the task's 16 query channels times their key clusters' s, in fp32
+    float qs[kAttnMaxRounds][16];
 #pragma unroll
     for (int r = 0; r < kAttnMaxRounds; ++r) {
         const int i = tid + r * kAttnBlock;
         const int ch = (i / LPH) * D + (i % LPH) * 16;
         const bool on = r < rounds && i < ntask;
-        qa[r][0] = on ? *reinterpret_cast<const u32x4*>(q + (int64_t)b * C + ch) : u32x4{0u, 0u, 0u, 0u};
-        qa[r][1] = on ? *reinterpret_cast<const u32x4*>(q + (int64_t)b * C + ch + 8) : u32x4{0u, 0u, 0u, 0u};
+        const int cc = on ? ch : 0;
+        const u32x4 q0 = *reinterpret_cast<const u32x4*>(q + (int64_t)b * C + cc);
+        const u32x4 q1 = *reinterpret_cast<const u32x4*>(q + (int64_t)b * C + cc + 8);
+        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 s4 = reinterpret_cast<const float4*>(tk.s + cc)[k];
+            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const half2_t h = __builtin_bit_cast(half2_t, qw[(4 * k + e) / 2]);
+                const float qf = (float)((4 * k + e) & 1 ? h.y : h.x);
+                qs[r][4 * k + e] = on ? qf * sv[e] : 0.0f;
+            }
+        }
     }
     tables(tk);
     run_rows(kp, [&](int t) {
@@ -207,13 +232,13 @@ __global__ __launch_bounds__(kAttnBlock) void kv_attn_chunk_kernel(
             const u32x4 x0 = *reinterpret_cast<const u32x4*>(xrow + ch * 2);
             const u32x4 x1 = *reinterpret_cast<const u32x4*>(xrow + ch * 2 + 16);
             const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            const uint32_t qs[8] = {qa[r][0].x, qa[r][0].y, qa[r][0].z, qa[r][0].w,
-                                    qa[r][1].x, qa[r][1].y, qa[r][1].z, qa[r][1].w};
             float s = 0.0f;
 #pragma unroll
-            for (int w = 0; w < 8; ++w)
-                s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qs[w]), __builtin_bit_cast(half2_t, xs[w]), s,
-                                           false);
+            for (int w = 0; w < 8; ++w) {
+                const half2_t hx = __builtin_bit_cast(half2_t, xs[w]);
+                s = __builtin_fmaf(qs[r][2 * w], (float)hx.x, s);
+                s = __builtin_fmaf(qs[r][2 * w + 1], (float)hx.y, s);
+            }
 #pragma unroll
             for (int o = 1; o < LPH; o <<= 1) s += __shfl_xor(s, o, 64);
             if (on && (i % LPH) == 0) S[t * H + i / LPH] = s * scale;
@@ -263,13 +288,18 @@ __global__ __launch_bounds__(kAttnBlock) void kv_attn_chunk_kernel(
             }
         }
     });
+    // each output channel's sum of p (q - z) times its value cluster's s
     float* op = o_part + ((int64_t)b * nch + kc) * C;
 #pragma unroll
     for (int u = 0; u < UPL; ++u) {
         const int oc = tid + u * kAttnBlock;
         if (oc < n_units) {
-            reinterpret_cast<float4*>(op + oc * 8)[0] = float4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
-            reinterpret_cast<float4*>(op + oc * 8)[1] = float4{acc[u][4], acc[u][5], acc[u][6], acc[u][7]};
+            const float4 s0 = reinterpret_cast<const float4*>(tv.s + oc * 8)[0];
+            const float4 s1 = reinterpret_cast<const float4*>(tv.s + oc * 8)[1];
+            reinterpret_cast<float4*>(op + oc * 8)[0] =
+                float4{acc[u][0] * s0.x, acc[u][1] * s0.y, acc[u][2] * s0.z, acc[u][3] * s0.w};
+            reinterpret_cast<float4*>(op + oc * 8)[1] =
+                float4{acc[u][4] * s1.x, acc[u][5] * s1.y, acc[u][6] * s1.z, acc[u][7] * s1.w};
         }
     }
 }
@@ -323,8 +353,9 @@ void kv_attention_geometry(int32_t T, int32_t C, int32_t D, int32_t& TC, int32_t
 }
 
 // Workspace: per-chunk outputs [B][nch][C] fp32, softmax statistics
-// [B][nch][H][2] fp32, then the K and V code tables (C x (2 + 4 + 4) bytes
-// each); every part starts on a 256-byte boundary.
+// [B][nch][H][2] fp32, then the K and V tables (C x (2 + 4 + 4) bytes each:
+// natural channel and z per code, s per natural channel); every part starts
+// on a 256-byte boundary.
 static int64_t up256(int64_t n) { return (n + 255) / 256 * 256; }
 
 int64_t kv_attention_workspace(int32_t B, int32_t T, int32_t C, int32_t D) {
