@@ -19,14 +19,13 @@
 //     padded to multiples of 32 codes, so a step never straddles clusters;
 //   - A (3/4/8-bit activation codes) and W' (3/4/8-bit weights) are fetched
 //     packed with buffer loads (scalar stage offsets; rows past M or N read
-//     as zero) about two stages ahead and staged in a double-buffered LDS
-//     tile.  W' is unpacked to int8 on the way in (row stride 144 B: the
-//     16-byte fragment reads of 8 consecutive lanes hit disjoint banks);
-//     4-bit codes stay packed in LDS (half the store bytes) and each wave
-//     unpacks its own fragments after reading them; 3/8-bit codes are
-//     unpacked on the way in.  The next stage's staging is interleaved with
-//     the current stage's MFMAs, and each stage's last MFMA step is deferred
-//     past the barrier to cover the next stage's first fragment reads;
+//     as zero) about two stages ahead, one staging piece per lane and MFMA
+//     step, and staged in a double-buffered LDS tile, both unpacked to int8
+//     on the way in (row stride 144 B: the 16-byte fragment reads of 8
+//     consecutive lanes hit disjoint banks).  The next stage's staging is
+//     interleaved with the current stage's MFMAs, and each stage's last MFMA
+//     step is deferred past the barrier to cover the next stage's first
+//     fragment reads;
 //   - one running int32 accumulator per MFMA tile for the whole K loop: at
 //     the last step of cluster c it is converted and added to fp32 out with
 //     weight d_c = s_c - s_(c+1) (summation by parts of sum_c s_c acc_c), so
@@ -46,7 +45,6 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 constexpr int GROUP_M = 8;
@@ -151,13 +149,10 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     constexpr int PA = CFG::PA, PB = CFG::PB, WN = CFG::WN;
     constexpr int NPIECE = PA + PB;
     static_assert(NPIECE <= SK, "one staged piece per step");
-    // 4-bit codes stay packed in LDS (rows of SK * 16 bytes, padded to
-    // SK * 16 + 8 so that the 8-byte fragment reads of 32 consecutive lanes
-    // hit 64 distinct banks) and are unpacked by each wave after reading
-    // its fragments: half the LDS store bytes of the unpacked tile
-    constexpr bool APACK = ABITS == 4;
-    constexpr int ALDSS = APACK ? SK * 16 + 8 : LDSS;
-    __shared__ __align__(16) int8_t As[2][BM * ALDSS];
+    // both operands are unpacked to int8 on their way into LDS (once per
+    // workgroup, where unpacking after the fragment reads would repeat it in
+    // each of the two waves that read a fragment)
+    __shared__ __align__(16) int8_t As[2][BM * LDSS];
     __shared__ __align__(16) int8_t Bs[2][BN * LDSS];
     constexpr int APIECE = 4 * ABITS, BPIECE = 4 * WBITS;           // bytes per 32 codes
 
@@ -205,7 +200,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     for (int i = 0; i < PA; ++i) {
         const int p = tid + i * NT, row = p / SK, part = p % SK;
         a_voff[i] = (uint32_t)(row * a_row_bytes + part * APIECE);
-        a_lds[i] = row * ALDSS + part * (APACK ? 16 : 32);
+        a_lds[i] = row * LDSS + part * 32;
         a_step[i] = part;
     }
 #pragma unroll
@@ -249,14 +244,8 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     auto put = [&](const Stage& S, int buf, int k) {
         uint32_t o[8];
         if (k < PA) {
-            if constexpr (APACK) {
-                int8_t* p = &As[buf][a_lds[k]];
-                reinterpret_cast<u32x2*>(p)[0] = u32x2{S.a[k][0], S.a[k][1]};
-                reinterpret_cast<u32x2*>(p)[1] = u32x2{S.a[k][2], S.a[k][3]};
-            } else {
-                unpack_act<ABITS>(S.a[k], o);
-                store32(&As[buf][a_lds[k]], o);
-            }
+            unpack_act<ABITS>(S.a[k], o);
+            store32(&As[buf][a_lds[k]], o);
         } else {
             unpack_wgt<WBITS>(S.b[k - PA], o);
             store32(&Bs[buf][b_lds[k - PA]], o);
@@ -287,7 +276,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
 
     // accumulator register r of this lane holds row (r/4)*8 + (lane/32)*4 + r%4, column lane%32
     const int row_l = (lane >> 5) * 4, col_l = lane & 31;
-    const int a_frag = (wm * 64 + (lane & 31)) * ALDSS + (lane >> 5) * (APACK ? 8 : 16);
+    const int a_frag = (wm * 64 + (lane & 31)) * LDSS + (lane >> 5) * 16;
     const int b_frag = (wn * 64 + (lane & 31)) * LDSS + (lane >> 5) * 16;
 
     int c = 0, c_end = __builtin_amdgcn_readfirstlane(end_l);
@@ -349,16 +338,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
         auto rd = [&](int slot, int ks) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-            {
-                if constexpr (APACK) {
-                    // 16 packed codes (byte i = c_i | c_(4+i) << 4) -> 16 int8 in code order
-                    const u32x2 d = *reinterpret_cast<const u32x2*>(&As[buf][a_frag + i * 32 * ALDSS + ks * 16]);
-                    af[slot][i] = v4i{(int)(d.x & 0x0F0F0F0Fu), (int)((d.x >> 4) & 0x0F0F0F0Fu),
-                                      (int)(d.y & 0x0F0F0F0Fu), (int)((d.y >> 4) & 0x0F0F0F0Fu)};
-                } else {
-                    af[slot][i] = *reinterpret_cast<const v4i*>(&As[buf][a_frag + i * 32 * LDSS + ks * 32]);
-                }
-            }
+                af[slot][i] = *reinterpret_cast<const v4i*>(&As[buf][a_frag + i * 32 * LDSS + ks * 32]);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 bf[slot][j] = *reinterpret_cast<const v4i*>(&Bs[buf][b_frag + j * 32 * LDSS + ks * 32]);
