@@ -44,8 +44,13 @@
  *     to back; row bytes = C * b / 8.
  *   SEG32 rows (LayerNorm output, GEMM input): cluster c starts at padded
  *     position off_c = sum_{c'<c} ceil(n_c'/32)*32 (n_c = cluster size) and is
- *     padded with code 0 up to a multiple of 32; K_pad = off_g; row bytes =
- *     K_pad * b / 8 (see rptq_codes_row_bytes).
+ *     padded with code 0 up to a multiple of 32; K_pad = off_g.  A row holds
+ *     K_pad * b / 8 bytes of codes, and rows are laid out with a pitch of
+ *     that size rounded up to a multiple of 64 bytes (rptq_codes_row_bytes),
+ *     so that the GEMM's 64-byte stage segments of a row never straddle two
+ *     64-byte memory sectors.  The bytes between the codes and the pitch are
+ *     neither written by the producers nor read by the GEMM.  Packed weights
+ *     use the same pitch (rptq_weights_row_bytes), with those bytes zero.
  *
  * Conventions for every entry point.
  *   - Pointers marked "device" are GPU memory owned by the caller (for
@@ -408,9 +413,11 @@ int rptq_pack_weights_out(const int8_t* wq, int32_t K, int32_t N, int32_t w_bits
 
 /* K_pad of the SEG32 layout; -1 on invalid bounds. */
 int32_t rptq_codes_kpad(const int32_t* bounds, int32_t g);
-/* SEG32 row stride in bytes for activation codes; -1 on invalid input. */
+/* SEG32 row pitch in bytes for activation codes (K_pad * bits / 8 rounded up
+   to a multiple of 64); -1 on invalid input. */
 int64_t rptq_codes_row_bytes(const int32_t* bounds, int32_t g, int32_t bits);
-/* Row stride of w_packed in bytes (K_pad * w_bits / 8); -1 on invalid input. */
+/* Row pitch of w_packed in bytes (K_pad * w_bits / 8 rounded up to a multiple
+   of 64); -1 on invalid input. */
 int64_t rptq_weights_row_bytes(const int32_t* bounds, int32_t g, int32_t w_bits);
 /* DENSE K/V row stride in bytes (C * bits / 8); -1 on invalid input. */
 int64_t rptq_kv_row_bytes(int32_t C, int32_t bits);

@@ -116,6 +116,21 @@ def _check(st: int, where: str):
         raise RptqError(st, where, lib().rptq_last_error().decode())
 
 
+def _need(t, nbytes: int, where: str, what: str):
+    """A caller's tensor must hold the bytes the call reads or writes through
+    its pointer (the C entry points take bare pointers and cannot check)."""
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise RptqError(RPTQ_ERR_INVALID_ARG, where, f"{what} holds {have} bytes, {nbytes} needed")
+
+
+def _codes_bytes(M: int, bounds, bits: int, where: str) -> int:
+    rb = rptq_codes_row_bytes(bounds, bits)
+    if rb < 0:
+        _check(RPTQ_ERR_INVALID_ARG, where)
+    return M * rb
+
+
 def _h(a, dtype):
     """Host numpy array of the given dtype, contiguous."""
     if isinstance(a, torch.Tensor):
@@ -190,6 +205,7 @@ def rptq_ln_reorder_quant(x, R, gamma_r, beta_r, bounds, s, z, bits, eps=1e-5,
         _check(RPTQ_ERR_INVALID_ARG, "rptq_codes_row_bytes")
     if out is None:
         out = _empty((M, rb), torch.uint8, x.device, stream)
+    _need(out, M * rb, "rptq_ln_reorder_quant", "out")
     st = lib().rptq_ln_reorder_quant(_dp(x), in_mode, M, K, _dp(gamma_r), _dp(beta_r), eps, _dp(R),
                                      _hp(b), b.size - 1, _hp(sh), _hp(zh), bits, _dp(out), _stream(stream))
     _check(st, "rptq_ln_reorder_quant")
@@ -220,6 +236,7 @@ def rptq_ln_reorder_quant_dynamic(x, R, gamma_r, beta_r, bounds, bits, eps=1e-5,
         z_out = _empty(max(g, 1), torch.int32, x.device, stream)
     if workspace is None:
         workspace = _empty(max(rptq_ln_dynamic_workspace_bytes(g), 16), torch.uint8, x.device, stream)
+    _need(out, M * rb, "rptq_ln_reorder_quant_dynamic", "out")
     st = lib().rptq_ln_reorder_quant_dynamic(_dp(x), in_mode, M, K, _dp(gamma_r), _dp(beta_r), eps, _dp(R),
                                              _hp(b), g, bits, _dp(out), _dp(s_out), _dp(z_out), _dp(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream))
@@ -235,6 +252,9 @@ def rptq_ln_reorder_quant_dynamic_noalloc(x, R, gamma_r, beta_r, bounds, bits, o
     allocated on the device.  Calls that may overlap on one GPU race."""
     M, K = x.shape
     b = _h(bounds, np.int32); g = b.size - 1
+    if M > 0:
+        _need(out, _codes_bytes(M, b, bits, "rptq_ln_reorder_quant_dynamic_noalloc"),
+              "rptq_ln_reorder_quant_dynamic_noalloc", "out")
     st = lib().rptq_ln_reorder_quant_dynamic_noalloc(_dp(x), in_mode, M, K, _dp(gamma_r), _dp(beta_r), eps,
                                                      _dp(R), _hp(b), g, bits, _dp(out), _dp(s_out), _dp(z_out),
                                                      _stream(stream))
@@ -246,6 +266,8 @@ def rptq_qgemm_dynamic(codes, M, K, N, bounds, s_dev, z_dev, a_bits, w_packed, w
                        stream=None):
     """rptq_qgemm with (s, z) as cuda tensors (fp32 [g], int32 [g])."""
     b = _h(bounds, np.int32)
+    _need(codes, _codes_bytes(M, b, a_bits, "rptq_qgemm_dynamic"), "rptq_qgemm_dynamic", "codes")
+    _need(w_packed, N * max(rptq_weights_row_bytes(b, w_bits), 0), "rptq_qgemm_dynamic", "w_packed")
     if out is None:
         out = _empty((M, N), torch.float32, codes.device, stream)
     st = lib().rptq_qgemm_dynamic(_dp(codes), M, K, N, _hp(b), b.size - 1, _dp(s_dev), _dp(z_dev), a_bits,
@@ -256,9 +278,11 @@ def rptq_qgemm_dynamic(codes, M, K, N, bounds, s_dev, z_dev, a_bits, w_packed, w
 
 def rptq_qgemm(codes, M, K, N, bounds, s, z, a_bits, w_packed, w_bits, s_w, colsum, out=None,
                acc_debug=None, stream=None):
-    """codes: cuda uint8 SEG32 [M][row_bytes]; w_packed: cuda uint8 [N][K_pad*w_bits/8];
+    """codes: cuda uint8 SEG32 [M][row_bytes]; w_packed: cuda uint8 [N][rptq_weights_row_bytes];
     s_w: cuda fp32 [N]; colsum: cuda int32 [g][N].  Returns Y cuda fp32 [M][N]."""
     b = _h(bounds, np.int32); sh = _h(s, np.float32); zh = _h(z, np.int32)
+    _need(codes, _codes_bytes(M, b, a_bits, "rptq_qgemm"), "rptq_qgemm", "codes")
+    _need(w_packed, N * max(rptq_weights_row_bytes(b, w_bits), 0), "rptq_qgemm", "w_packed")
     if out is None:
         out = _empty((M, N), torch.float32, codes.device, stream)
     st = lib().rptq_qgemm(_dp(codes), M, K, N, _hp(b), b.size - 1, _hp(sh), _hp(zh), a_bits, _dp(w_packed),
@@ -275,11 +299,14 @@ def rptq_qgemm_quant(codes, M, K, N_pad, bounds, s, z, a_bits, w_packed, w_bits,
     [M][N_pad]) receives the activated output before quantization."""
     b = _h(bounds, np.int32); sh = _h(s, np.float32); zh = _h(z, np.int32)
     ob = _h(out_bounds, np.int32); osh = _h(out_s, np.float32); ozh = _h(out_z, np.int32)
+    _need(codes, _codes_bytes(M, b, a_bits, "rptq_qgemm_quant"), "rptq_qgemm_quant", "codes")
+    _need(w_packed, N_pad * max(rptq_weights_row_bytes(b, w_bits), 0), "rptq_qgemm_quant", "w_packed")
+    orb = rptq_codes_row_bytes(ob, out_bits)
+    if orb < 0:
+        _check(RPTQ_ERR_INVALID_ARG, "rptq_codes_row_bytes")
     if out is None:
-        rb = rptq_codes_row_bytes(ob, out_bits)
-        if rb < 0:
-            _check(RPTQ_ERR_INVALID_ARG, "rptq_codes_row_bytes")
-        out = _empty((M, rb), torch.uint8, codes.device, stream)
+        out = _empty((M, orb), torch.uint8, codes.device, stream)
+    _need(out, M * orb, "rptq_qgemm_quant", "out")
     st = lib().rptq_qgemm_quant(_dp(codes), M, K, N_pad, _hp(b), b.size - 1, _hp(sh), _hp(zh), a_bits,
                                 _dp(w_packed), w_bits, _dp(s_w), _dp(colsum), act, _hp(ob), ob.size - 1,
                                 _hp(osh), _hp(ozh), out_bits, _dp(out), _dp(y_out), _stream(stream))
@@ -385,7 +412,7 @@ def rptq_quantize_weights(W, w_bits):
 
 
 def rptq_pack_weights(wq, R, bounds, w_bits):
-    """Host.  Returns (w_packed uint8 [N][K_pad*w_bits/8], colsum int32 [g][N])."""
+    """Host.  Returns (w_packed uint8 [N][rptq_weights_row_bytes], colsum int32 [g][N])."""
     wqh = _h(wq, np.int8)
     K, N = wqh.shape
     Rh = None if R is None else _h(R, np.int32)
@@ -400,7 +427,7 @@ def rptq_pack_weights(wq, R, bounds, w_bits):
 
 
 def rptq_pack_weights_out(wq, R, bounds, w_bits, R_out, out_bounds, s_w):
-    """Host.  Returns (w_packed uint8 [N_pad][K_pad*w_bits/8], colsum int32
+    """Host.  Returns (w_packed uint8 [N_pad][rptq_weights_row_bytes], colsum int32
     [g][N_pad], s_w_out fp32 [N_pad]) with the output features in the next
     layer's padded order."""
     wqh = _h(wq, np.int8)

@@ -378,9 +378,10 @@ __global__ __launch_bounds__(kMaxBlock) void ln_reorder_quant_kernel(
         }
         if constexpr (DM != kRanges) {
             __syncthreads();
-            // 3-bit rows are a multiple of 12 bytes: 4-byte stores
-            store_row_chunks<BITS != 3, chunks_for<BITS != 3>(UPL * BITS)>(codes + row * row_bytes,
-                                                                           row < M ? row_bytes : 0, orow);
+            // row_bytes is the row pitch; the row's K_pad * BITS / 8 bytes are
+            // stored (3-bit rows are a multiple of 12 bytes: 4-byte stores)
+            store_row_chunks<BITS != 3, chunks_for<BITS != 3>(UPL * BITS)>(
+                codes + row * row_bytes, row < M ? (int64_t)ca.K_pad * BITS / 8 : 0, orow);
         }
     };
 

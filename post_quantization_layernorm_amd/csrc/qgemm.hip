@@ -361,10 +361,10 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
             // the staging stores (so the reads never wait behind them)
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write

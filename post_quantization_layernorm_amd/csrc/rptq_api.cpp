@@ -148,14 +148,19 @@ int32_t rptq_codes_kpad(const int32_t* bounds, int32_t g) {
     return kpad_of(bounds, g);
 }
 
+// Row pitch of SEG32 codes and packed weights: the K_pad * bits / 8 bytes of
+// a row, padded to a multiple of 64 bytes so that the GEMM's 64-byte stage
+// segments of a row never straddle two 64-byte sectors.
+static int64_t seg32_pitch(int32_t kpad, int32_t bits) { return ((int64_t)kpad * bits / 8 + 63) / 64 * 64; }
+
 int64_t rptq_codes_row_bytes(const int32_t* bounds, int32_t g, int32_t bits) {
     if (!valid_bits(bits) || check_bounds(bounds, g, -1) != RPTQ_OK) return -1;
-    return (int64_t)kpad_of(bounds, g) * bits / 8;
+    return seg32_pitch(kpad_of(bounds, g), bits);
 }
 
 int64_t rptq_weights_row_bytes(const int32_t* bounds, int32_t g, int32_t w_bits) {
     if (!valid_wbits(w_bits) || check_bounds(bounds, g, -1) != RPTQ_OK) return -1;
-    return (int64_t)kpad_of(bounds, g) * w_bits / 8;
+    return seg32_pitch(kpad_of(bounds, g), w_bits);
 }
 
 int64_t rptq_kv_row_bytes(int32_t C, int32_t bits) {
@@ -188,7 +193,7 @@ int rptq_ln_reorder_quant(const void* x, int32_t in_mode, int64_t M, int32_t K,
         (in_mode == RPTQ_IN_FP16_RAW && (!aligned16(gamma_r) || !aligned16(beta_r) || (R && !aligned16(R)))))
         return fail(RPTQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
     const ClusterArgs ca = make_cluster_args(bounds, g, s, z, bits, true);
-    const int64_t row_bytes = (int64_t)ca.K_pad * bits / 8;
+    const int64_t row_bytes = seg32_pitch(ca.K_pad, bits);
     return hip_status(launch_ln_reorder_quant(x, in_mode, M, K, gamma_r, beta_r, eps,
                                               in_mode == RPTQ_IN_FP16_RAW ? R : nullptr, ca, row_bytes,
                                               codes, (hipStream_t)stream),
@@ -240,7 +245,7 @@ static int ln_dynamic_common(const void* x, int32_t in_mode, int64_t M, int32_t 
     int32_t z0[kMaxClusters];
     for (int c = 0; c < g; ++c) { s1[c] = 1.0f; z0[c] = 0; }
     const ClusterArgs ca = make_cluster_args(bounds, g, s1, z0, bits, true);
-    const int64_t row_bytes = (int64_t)ca.K_pad * bits / 8;
+    const int64_t row_bytes = seg32_pitch(ca.K_pad, bits);
     return hip_status(launch_ln_reorder_quant_dynamic(x, in_mode, M, K, gamma_r, beta_r, eps,
                                                       in_mode == RPTQ_IN_FP16_RAW ? R : nullptr, ca, row_bytes,
                                                       codes, s_out, z_out, static_cast<float*>(workspace),
@@ -322,8 +327,8 @@ static int qgemm_common(const uint8_t* codes, int64_t M, int32_t K, int32_t N, c
         }
     }
     ga.nsteps = steps;
-    const int64_t a_row_bytes = (int64_t)steps * 32 * a_bits / 8;
-    const int64_t w_row_bytes = (int64_t)steps * 32 * w_bits / 8;
+    const int64_t a_row_bytes = seg32_pitch(steps * 32, a_bits);
+    const int64_t w_row_bytes = seg32_pitch(steps * 32, w_bits);
     return hip_status(launch_qgemm(codes, M, N, a_row_bytes, a_bits, w_packed, w_row_bytes, w_bits, ga, s_w,
                                    colsum, Y, acc_debug, qo, qc, (hipStream_t)stream),
                       what);
@@ -366,7 +371,7 @@ int rptq_qgemm_quant(const uint8_t* codes, int64_t M, int32_t K, int32_t N_pad, 
         return fail(RPTQ_ERR_INVALID_ARG, "N_pad = %d is not the output layout's K_pad %d", N_pad,
                     kpad_of(out_bounds, out_g));
     if (M > 0 && !out_codes) return fail(RPTQ_ERR_INVALID_ARG, "out_codes must be non-NULL");
-    QuantOutArgs qo{out_codes, (int64_t)N_pad * out_bits / 8, act};
+    QuantOutArgs qo{out_codes, seg32_pitch(N_pad, out_bits), act};
     const ClusterArgs qc = make_cluster_args(out_bounds, out_g, out_s, out_z, out_bits, true);
     return qgemm_common(codes, M, K, N_pad, bounds, g, s, z, a_bits, w_packed, w_bits, s_w, colsum, Y, nullptr,
                         qo, qc, stream, "rptq_qgemm_quant launch");
@@ -640,7 +645,7 @@ int rptq_pack_weights(const int8_t* wq, int32_t K, int32_t N, int32_t w_bits, co
     if (st) return st;
     const int qm = (1 << (w_bits - 1)) - 1;
     const int32_t kp = kpad_of(bounds, g);
-    const int64_t rb = (int64_t)kp * w_bits / 8;
+    const int64_t rb = seg32_pitch(kp, w_bits), data_bytes = (int64_t)kp * w_bits / 8;
     // padded position -> natural row (-1 for pad)
     std::vector<int32_t> src(kp, -1);
     std::vector<int32_t> clus(kp, 0);
@@ -671,6 +676,7 @@ int rptq_pack_weights(const int8_t* wq, int32_t K, int32_t N, int32_t w_bits, co
                     colsum[(int64_t)clus[p] * N + n] += col[p];
                 }
                 uint8_t* dst = w_packed + (int64_t)n * rb;
+                std::memset(dst + data_bytes, 0, (size_t)(rb - data_bytes));
                 if (w_bits == 8) {
                     for (int32_t p = 0; p < kp; ++p) dst[p] = (uint8_t)col[p];
                 } else if (w_bits == 3) {

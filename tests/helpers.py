@@ -72,3 +72,24 @@ def dev(a, dtype=None):
 def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64); b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def seg32_pitch(bounds, bits) -> int:
+    """The library's row pitch of SEG32 codes: the oracle's row bytes
+    (K_pad * bits / 8) rounded up to a multiple of 64."""
+    return (orc.seg32_row_bytes(bounds, bits) + 63) // 64 * 64
+
+
+def code_bytes(codes, bounds, bits) -> np.ndarray:
+    """Host copy of the code bytes of pitched SEG32 rows (a GPU tensor or an
+    array), without the pitch's tail: comparable with the oracle's rows."""
+    a = codes.cpu().numpy() if hasattr(codes, "cpu") else np.asarray(codes)
+    return np.ascontiguousarray(a[:, :orc.seg32_row_bytes(bounds, bits)])
+
+
+def pitched(codes_o, bounds, bits) -> np.ndarray:
+    """The oracle's SEG32 rows laid out at the library's row pitch (zero tail),
+    as the GEMM reads them."""
+    out = np.zeros((codes_o.shape[0], seg32_pitch(bounds, bits)), np.uint8)
+    out[:, :codes_o.shape[1]] = codes_o
+    return out

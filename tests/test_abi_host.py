@@ -284,8 +284,13 @@ def test_status_strings_and_sizes(P):
     assert L.rptq_status_string(0) == b"ok" and L.rptq_status_string(-4) == b"HIP error"
     b = np.array([0, 1, 32, 64, 97, 192], np.int32)
     assert P.rptq_codes_kpad(b) == 256
-    assert P.rptq_codes_row_bytes(b, 3) == 96 and P.rptq_codes_row_bytes(b, 4) == 128
+    # row pitch: K_pad * b / 8 bytes rounded up to a multiple of 64
+    assert P.rptq_codes_row_bytes(b, 3) == 128 and P.rptq_codes_row_bytes(b, 4) == 128
     assert P.rptq_codes_row_bytes(b, 8) == 256 and P.rptq_weights_row_bytes(b, 4) == 128
+    b2 = np.array([0, 9216], np.int32)                      # K_pad 9216: 4-bit rows of 4608 B
+    assert P.rptq_codes_row_bytes(b2, 4) == 4608 and P.rptq_codes_row_bytes(b2, 3) == 3456
+    b3 = np.array([0, 9, 9216], np.int32)                   # K_pad 9248: 4624 B -> 4672, 3468 B -> 3520
+    assert P.rptq_codes_row_bytes(b3, 4) == 4672 and P.rptq_weights_row_bytes(b3, 3) == 3520
     assert P.rptq_codes_row_bytes(b, 5) == -1
     assert P.rptq_kv_row_bytes(9216, 3) == 3456 and P.rptq_kv_row_bytes(72, 3) == -1
 
@@ -326,10 +331,11 @@ def test_host_pack_weights_reorders_pads_and_sums(P, orc, wb):
     bounds = np.array([0, 1, 33, 64, 100], np.int32)
     wp, cs = P.rptq_pack_weights(wq, R, bounds, wb)
     kp = orc.seg32_kpad(bounds)
-    assert wp.shape == (N, kp * wb // 8)
+    data = kp * wb // 8
+    assert wp.shape == (N, (data + 63) // 64 * 64) and not wp[:, data:].any()   # 64-byte pitch, zero tail
     # the packed rows use the same group layout as activation codes (two's
     # complement nibbles); decode with the oracle's unpacker
-    codes = orc.unpack_dense(wp, kp, wb).astype(np.int16)
+    codes = orc.unpack_dense(np.ascontiguousarray(wp[:, :data]), kp, wb).astype(np.int16)
     half = 2 ** (wb - 1)
     codes = np.where(codes >= half, codes - 2 * half, codes)
     dense, pad = orc.unpack_seg32(orc.pack_dense(np.zeros((N, kp), np.uint8), 8), K, bounds, 8, return_pad=True)
@@ -367,7 +373,7 @@ int main(void) {
     const int32_t b2[3] = {0, 16, 64};
     int bad = 0;
     if (rptq_codes_kpad(bounds, 5) != 256) bad |= 1;
-    if (rptq_codes_row_bytes(bounds, 5, 3) != 96) bad |= 2;
+    if (rptq_codes_row_bytes(bounds, 5, 3) != 128) bad |= 2;
     if (rptq_kv_row_bytes(9216, 3) != 3456) bad |= 4;
     if (rptq_ln_dynamic_workspace_bytes(32) != 262144) bad |= 8;
     /* argument errors come back before any HIP call, with a message */

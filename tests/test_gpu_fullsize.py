@@ -12,7 +12,7 @@ import pytest
 
 import oracle as orc
 import synthetic
-from helpers import dev, rel_l2
+from helpers import code_bytes, dev, pitched, rel_l2
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -72,7 +72,7 @@ def test_fc1_fullsize_ln_quant_every_row(P, fc1, ab):
     _say("ln", ab)
     xd = dev(fc1["x"].view(np.int16)).view(torch.float16)
     codes = P.rptq_ln_reorder_quant(xd, dev(R), dev(fc1["gamma"][R]), dev(fc1["beta"][R]), bounds, s, z, ab)
-    got = codes.cpu().numpy()
+    got = code_bytes(codes, bounds, ab)
     del codes, xd
     want = orc.ln_reorder_quant(fc1["x"], fc1["gamma"], fc1["beta"], 1e-5, R, bounds, s, z, ab)
     for r0 in range(0, M, 4096):                 # unpacked in slices to bound host memory
@@ -93,7 +93,7 @@ def test_fc1_fullsize_gemm_sampled(P, fc1, ab, wb):
     codes_o = orc.ln_reorder_quant(fc1["x"], fc1["gamma"], fc1["beta"], 1e-5, R, bounds, s, z, ab)
     wp, cs = P.rptq_pack_weights(Wq, R, bounds, wb)
     wp, cs, sw = dev(wp), dev(cs), dev(s_w)
-    cd = dev(codes_o)
+    cd = dev(pitched(codes_o, bounds, ab))
     Y = P.rptq_qgemm(cd, M, K, N, bounds, s, z, ab, wp, wb, sw, cs)
     # 256 evenly spaced rows (two in every 128-row tile-row) over the full N
     rows = _spread_rows(M, 256)
@@ -106,8 +106,8 @@ def test_fc1_fullsize_gemm_sampled(P, fc1, ab, wb):
         assert rel_l2(Ys[i], Y_o[i]) <= 1e-3, rows[i]
     # int32 accumulators bit-exact over full K and N on two 64-row slices
     # (a full-size debug buffer would be g x M x N x 4 bytes), in two places
-    # of the batch (row offsets keep the code rows 16-byte aligned at 3 bits)
-    for r0 in (4096, M - 64 - 36):
+    # of the batch (the middle and the last tile-row)
+    for r0 in (4096, M - 64):
         acc = torch.zeros((g, 64, N), dtype=torch.int32, device="cuda")
         P.rptq_qgemm(cd[r0:r0 + 64], 64, K, N, bounds, s, z, ab, wp, wb, sw, cs, acc_debug=acc)
         q64 = orc.unpack_seg32(codes_o[r0:r0 + 64], K, bounds, ab)
@@ -134,7 +134,8 @@ def test_fc1_fullsize_dynamic_sampled(P, fc1):
     sh, zh = sd.cpu().numpy(), zd.cpu().numpy()
     assert np.abs(sh.astype(np.float64) / s_o - 1.0).max() <= 1e-5
     assert np.abs(zh.astype(np.int64) - z_o).max() <= 1
-    qg, pad = orc.unpack_seg32(codes[torch.from_numpy(ROWS).cuda()].cpu().numpy(), K, bounds, 4, return_pad=True)
+    qg, pad = orc.unpack_seg32(code_bytes(codes[torch.from_numpy(ROWS).cuda()], bounds, 4), K, bounds, 4,
+                               return_pad=True)
     qw = orc.unpack_seg32(want, K, bounds, 4)
     d = np.abs(qg.astype(np.int32) - qw.astype(np.int32))
     assert not pad.any()
@@ -146,7 +147,7 @@ def test_fc1_fullsize_dynamic_sampled(P, fc1):
     Ys = P.rptq_qgemm(codes, M, K, N, bounds, sh, zh, 4, wp, 4, sw, cs)
     assert torch.equal(Y, Ys)
     del Ys
-    q = orc.unpack_seg32(codes[torch.from_numpy(ROWS).cuda()].cpu().numpy(), K, bounds, 4)
+    q = orc.unpack_seg32(code_bytes(codes[torch.from_numpy(ROWS).cuda()], bounds, 4), K, bounds, 4)
     Y_o = orc.qgemm(q, Wq, R, bounds, sh, zh, s_w)
     assert rel_l2(Y[torch.from_numpy(ROWS).cuda()].cpu().numpy(), Y_o) <= 1e-3
 
@@ -234,7 +235,7 @@ def test_layer_fullsize_sampled(P, name, ab):
     # compared with the oracle's codes
     xd = dev(x.view(np.int16)).view(torch.float16)
     codes = P.rptq_ln_reorder_quant(xd, dev(R), dev(gamma[R]), dev(beta[R]), bounds, s, z, ab)
-    got = codes.cpu().numpy()
+    got = code_bytes(codes, bounds, ab)
     codes_o = orc.ln_reorder_quant(x, gamma, beta, 1e-5, R, bounds, s, z, ab)
     qg, pad = orc.unpack_seg32(got, K, bounds, ab, return_pad=True)
     qw = orc.unpack_seg32(codes_o, K, bounds, ab)
@@ -246,7 +247,7 @@ def test_layer_fullsize_sampled(P, name, ab):
     # the GEMM over every row, on the oracle's codes
     wp, cs = P.rptq_pack_weights(Wq, R, bounds, wb)
     wp, cs, sw = dev(wp), dev(cs), dev(s_w)
-    cd = dev(codes_o)
+    cd = dev(pitched(codes_o, bounds, ab))
     Y = P.rptq_qgemm(cd, M, K, N, bounds, s, z, ab, wp, wb, sw, cs)
     Ys = Y[torch.from_numpy(rows).cuda()].cpu().numpy()
     del Y

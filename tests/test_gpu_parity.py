@@ -7,7 +7,7 @@ import pytest
 
 import oracle as orc
 import synthetic
-from helpers import dev, explicit_case, layer_case, rel_l2
+from helpers import code_bytes, dev, explicit_case, layer_case, pitched, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -100,7 +100,7 @@ def test_ln_quant_only_mode_bit_exact(P, bits, shape):
     got = P.rptq_ln_reorder_quant(dev(y), None, None, None, c.bounds, c.s, c.z, bits,
                                   in_mode=P.RPTQ_IN_FP32_NORMALIZED)
     torch.cuda.synchronize()
-    assert np.array_equal(got.cpu().numpy(), want)
+    assert np.array_equal(code_bytes(got, c.bounds, bits), want)
 
 
 def _fused(P, c, bits, eps=1e-5):
@@ -116,7 +116,7 @@ def test_ln_fused_codes_within_tolerance(P, bits, shape):
     _say("ln fused", bits, shape)
     c = layer_case(M, K, 8, g, bits, seed=K + bits, outlier_frac=frac, range_ratio=rr, with_weights=False)
     want = orc.ln_reorder_quant(c.x, c.gamma, c.beta, 1e-5, c.R, c.bounds, c.s, c.z, bits)
-    got = _fused(P, c, bits).cpu().numpy()
+    got = code_bytes(_fused(P, c, bits), c.bounds, bits)
     qg, pad_g = orc.unpack_seg32(got, K, c.bounds, bits, return_pad=True)
     qw = orc.unpack_seg32(want, K, c.bounds, bits)
     assert not pad_g.any()
@@ -141,8 +141,8 @@ def test_ln_fused_edge_rows(P):
     s, z = orc.cluster_params(mx, mn, None, bounds, 4)
     want = orc.ln_reorder_quant(x, gamma, beta, 1e-5, None, bounds, s, z, 4)
     for M in (1, 5):
-        got = P.rptq_ln_reorder_quant(dev(x[:M].view(np.int16)).view(torch.float16), None, dev(gamma), dev(beta),
-                                      bounds, s, z, 4).cpu().numpy()
+        got = code_bytes(P.rptq_ln_reorder_quant(dev(x[:M].view(np.int16)).view(torch.float16), None, dev(gamma),
+                                                 dev(beta), bounds, s, z, 4), bounds, 4)
         qg = orc.unpack_seg32(got, K, bounds, 4).astype(np.int32)
         qw = orc.unpack_seg32(want[:M], K, bounds, 4).astype(np.int32)
         assert np.abs(qg - qw).max() <= 1 and (qg != qw).mean() <= 1e-3
@@ -185,7 +185,7 @@ def test_ln_dynamic_quant_only_bit_exact(P, bits, shape):
         torch.cuda.synchronize()
         assert np.array_equal(sd.cpu().numpy(), s_o)
         assert np.array_equal(zd.cpu().numpy(), z_o)
-        assert np.array_equal(got.cpu().numpy(), want)
+        assert np.array_equal(code_bytes(got, c.bounds, bits), want)
 
 
 @pytest.mark.parametrize("bits", [3, 4, 8])
@@ -204,7 +204,7 @@ def test_ln_dynamic_fused_within_tolerance(P, bits, shape):
     sg, zg = sd.cpu().numpy(), zd.cpu().numpy()
     assert np.abs(sg.astype(np.float64) / s_o - 1.0).max() <= 1e-5
     assert np.abs(zg.astype(np.int64) - z_o).max() <= 1
-    qg, pad = orc.unpack_seg32(got.cpu().numpy(), K, c.bounds, bits, return_pad=True)
+    qg, pad = orc.unpack_seg32(code_bytes(got, c.bounds, bits), K, c.bounds, bits, return_pad=True)
     qw = orc.unpack_seg32(want, K, c.bounds, bits)
     assert not pad.any()
     d = np.abs(qg.astype(np.int32) - qw.astype(np.int32))
@@ -228,7 +228,7 @@ def test_qgemm_dynamic(P, ab, wb):
     Y_s = P.rptq_qgemm(codes, M, K, N, c.bounds, sh, zh, ab, wp, wb, sw, cs)
     torch.cuda.synchronize()
     assert torch.equal(Y, Y_s)
-    q = orc.unpack_seg32(codes.cpu().numpy(), K, c.bounds, ab)
+    q = orc.unpack_seg32(code_bytes(codes, c.bounds, ab), K, c.bounds, ab)
     Y_o = orc.qgemm(q, c.Wq, c.R, c.bounds, sh, zh, c.s_w)
     assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
 
@@ -272,12 +272,12 @@ def test_qgemm_accumulators_bit_exact_and_y(P, case):
     Y_o, acc_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w, return_acc=True)
     wp, cs, sw = _gemm_inputs(P, c)
     acc = torch.full((g, M, N), -7, dtype=torch.int32, device="cuda")
-    Y = P.rptq_qgemm(dev(codes), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs, acc_debug=acc)
+    Y = P.rptq_qgemm(dev(pitched(codes, c.bounds, ab)), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs, acc_debug=acc)
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy(), acc_o)
     assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
     # the debug buffer does not change Y
-    Y2 = P.rptq_qgemm(dev(codes), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs)
+    Y2 = P.rptq_qgemm(dev(pitched(codes, c.bounds, ab)), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs)
     assert torch.equal(Y, Y2)
 
 
@@ -295,12 +295,12 @@ def test_qgemm_many_tiles_bit_exact(P, case):
     Y_o, acc_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w, return_acc=True)
     wp, cs, sw = _gemm_inputs(P, c)
     acc = torch.full((g, M, N), -7, dtype=torch.int32, device="cuda")
-    Y = P.rptq_qgemm(dev(codes), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs, acc_debug=acc)
+    Y = P.rptq_qgemm(dev(pitched(codes, c.bounds, ab)), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs, acc_debug=acc)
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy(), acc_o)
     del acc
     assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
-    Y2 = P.rptq_qgemm(dev(codes), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs)
+    Y2 = P.rptq_qgemm(dev(pitched(codes, c.bounds, ab)), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs)
     assert torch.equal(Y, Y2)
 
 
@@ -316,7 +316,7 @@ def test_qgemm_ragged_clusters(P, bounds, ab, wb):
     Y_o, acc_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w, return_acc=True)
     wp, cs, sw = _gemm_inputs(P, c)
     acc = torch.zeros((c.g, c.M, c.N), dtype=torch.int32, device="cuda")
-    Y = P.rptq_qgemm(dev(codes), c.M, c.K, c.N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs, acc_debug=acc)
+    Y = P.rptq_qgemm(dev(pitched(codes, c.bounds, ab)), c.M, c.K, c.N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs, acc_debug=acc)
     assert np.array_equal(acc.cpu().numpy(), acc_o)
     assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
 
@@ -355,9 +355,9 @@ def test_qgemm_quant_output(P, ab, wb, ob, act, N):
     wp, cs, swo = P.rptq_pack_weights_out(c.Wq, c.R, c.bounds, wb, R2, b2, c.s_w)
     npad = orc.seg32_kpad(b2)
     yd = torch.full((M, npad), 7.0, dtype=torch.float32, device="cuda")
-    got = P.rptq_qgemm_quant(dev(codes), M, K, npad, c.bounds, c.s, c.z, ab, dev(wp), wb, dev(swo), dev(cs), act,
-                             b2, s2, z2, ob, y_out=yd)
-    got = got.cpu().numpy(); yg = yd.cpu().numpy()
+    got = P.rptq_qgemm_quant(dev(pitched(codes, c.bounds, ab)), M, K, npad, c.bounds, c.s, c.z, ab, dev(wp), wb,
+                             dev(swo), dev(cs), act, b2, s2, z2, ob, y_out=yd)
+    got = code_bytes(got, b2, ob); yg = yd.cpu().numpy()
     # padded position of each real output channel (in R2 order)
     pos = np.concatenate([orc.seg32_kpad(b2[:c2 + 1]) + np.arange(b2[c2 + 1] - b2[c2]) for c2 in range(g2)])
     real = np.zeros(npad, bool); real[pos] = True
@@ -442,9 +442,10 @@ def test_hot_path_replays_from_a_hip_graph(P):
     xd = dev(c.x.view(np.int16)).view(torch.float16)
     Rd, gr, br = dev(c.R), dev(c.gamma[c.R]), dev(c.beta[c.R])
     wp, cs, sw = _gemm_inputs(P, c)
-    rb = orc.seg32_row_bytes(c.bounds, ab)
-    codes = torch.empty((M, rb), dtype=torch.uint8, device="cuda")
-    codes_d = torch.empty_like(codes)
+    rb = P.rptq_codes_row_bytes(c.bounds, ab)
+    # zero-filled: the rows' pitch tails are never written, by eager runs or replays
+    codes = torch.zeros((M, rb), dtype=torch.uint8, device="cuda")
+    codes_d = torch.zeros_like(codes)
     Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     Yd = torch.empty_like(Y)
     sd = torch.empty(g, dtype=torch.float32, device="cuda")
@@ -540,13 +541,13 @@ def test_smallest_layer(P, bits, bounds):
     want = orc.pack_seg32(orc.quantize(y, c.bounds, c.s, c.z, bits), c.bounds, bits)
     got = P.rptq_ln_reorder_quant(dev(y), None, None, None, c.bounds, c.s, c.z, bits,
                                   in_mode=P.RPTQ_IN_FP32_NORMALIZED)
-    assert np.array_equal(got.cpu().numpy(), want)
+    assert np.array_equal(code_bytes(got, c.bounds, bits), want)
     wd, sd_o, zd_o = orc.quantize_dynamic(y, c.bounds, bits)
     gd, sd, zd = P.rptq_ln_reorder_quant_dynamic(dev(y), None, None, None, c.bounds, bits,
                                                  in_mode=P.RPTQ_IN_FP32_NORMALIZED)
-    assert np.array_equal(gd.cpu().numpy(), wd)
+    assert np.array_equal(code_bytes(gd, c.bounds, bits), wd)
     assert np.array_equal(sd.cpu().numpy(), sd_o) and np.array_equal(zd.cpu().numpy(), zd_o)
-    fused = _fused(P, c, bits).cpu().numpy()
+    fused = code_bytes(_fused(P, c, bits), c.bounds, bits)
     qf = orc.unpack_seg32(fused, K, c.bounds, bits).astype(np.int32)
     qo = orc.unpack_seg32(orc.ln_reorder_quant(c.x, c.gamma, c.beta, 1e-5, c.R, c.bounds, c.s, c.z, bits),
                           K, c.bounds, bits).astype(np.int32)
@@ -555,7 +556,8 @@ def test_smallest_layer(P, bits, bounds):
     Y_o, acc_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w, return_acc=True)
     wp, cs, sw = _gemm_inputs(P, c)
     acc = torch.zeros((c.g, M, N), dtype=torch.int32, device="cuda")
-    Y = P.rptq_qgemm(dev(want), M, K, N, c.bounds, c.s, c.z, bits, wp, 4, sw, cs, acc_debug=acc)
+    Y = P.rptq_qgemm(dev(pitched(want, c.bounds, bits)), M, K, N, c.bounds, c.s, c.z, bits, wp, 4, sw, cs,
+                     acc_debug=acc)
     assert np.array_equal(acc.cpu().numpy(), acc_o)
     assert rel_l2(Y.cpu().numpy(), Y_o) <= 1e-3
     Yd = P.rptq_qgemm_dynamic(gd, M, K, N, c.bounds, sd, zd, bits, wp, 4, sw, cs)

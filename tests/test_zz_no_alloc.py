@@ -6,7 +6,7 @@ still holds the first call's partials."""
 import numpy as np
 import pytest
 
-from helpers import dev, layer_case
+from helpers import code_bytes, dev, layer_case
 
 pytestmark = pytest.mark.gpu
 
@@ -30,13 +30,15 @@ def _run_both(P, M, K, g, bits, seed):
     gr, br = dev(c.gamma[c.R]), dev(c.beta[c.R])
     ref = P.rptq_ln_reorder_quant_dynamic(x, R, gr, br, c.bounds, bits)
     rb = P.rptq_codes_row_bytes(c.bounds, bits)
-    # outputs pre-filled with a pattern the kernels must overwrite
+    # outputs pre-filled with a pattern the kernels must overwrite (the code
+    # bytes of each row; the tail of the row pitch is not written)
     out = torch.full((M, rb), 0xA5, dtype=torch.uint8, device="cuda")
     s_out = torch.full((g,), -1.0, dtype=torch.float32, device="cuda")
     z_out = torch.full((g,), -7, dtype=torch.int32, device="cuda")
     got = P.rptq_ln_reorder_quant_dynamic_noalloc(x, R, gr, br, c.bounds, bits, out, s_out, z_out)
     torch.cuda.synchronize()
-    for a, b in zip(got, ref):
+    assert np.array_equal(code_bytes(got[0], c.bounds, bits), code_bytes(ref[0], c.bounds, bits))
+    for a, b in zip(got[1:], ref[1:]):
         assert torch.equal(a, b)
     return got
 
