@@ -3,7 +3,9 @@
 
 Each ``rptq_*`` function here has the name of the C entry point it wraps and
 only marshals arguments: torch tensors supply device memory and the current
-HIP stream, small host arrays (bounds, s, z) are passed as numpy arrays.
+HIP stream, small host arrays (bounds, s, z) are passed as numpy arrays, and
+caller-supplied tensors are checked to be large enough for the rows the call
+touches (codes and packed weights at their 64-byte row pitch).
 Every step of the hot path runs in the library's HIP kernels; there is no
 fallback -- if the library is missing or fails, the call raises.
 

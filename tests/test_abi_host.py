@@ -431,3 +431,21 @@ def test_ln_reorder_quant_dynamic_noalloc_rejects(P, kw, status):
     the workspace) before any HIP call."""
     assert _ln_dyn_noalloc(P, **kw) == status
     assert P.lib().rptq_last_error().decode()
+
+
+def test_binding_rejects_tensors_smaller_than_the_row_pitch(P):
+    """The C entry points take bare pointers; the binding checks that a
+    caller's tensor holds the rows the call touches at their 64-byte pitch
+    (here a code array laid out without the pitch) before any launch."""
+    import torch
+    b = np.array([0, 40, 100], np.int32)                 # K_pad 128: 64-byte rows at 4 bits, 48 at 3
+    s, z = np.ones(2, np.float32), np.zeros(2, np.int32)
+    wp = torch.zeros((8, P.rptq_weights_row_bytes(b, 4)), dtype=torch.uint8)
+    sw, cs = torch.zeros(8), torch.zeros((2, 8), dtype=torch.int32)
+    with pytest.raises(P.RptqError, match="codes holds"):
+        P.rptq_qgemm(torch.zeros((3, 48), dtype=torch.uint8), 3, 100, 8, b, s, z, 3, wp, 4, sw, cs)
+    with pytest.raises(P.RptqError, match="w_packed holds"):
+        P.rptq_qgemm(torch.zeros((3, 64), dtype=torch.uint8), 3, 100, 8, b, s, z, 4, wp[:7], 4, sw, cs)
+    x = torch.zeros((3, 100), dtype=torch.float16)
+    with pytest.raises(P.RptqError, match="out holds"):
+        P.rptq_ln_reorder_quant(x, None, None, None, b, s, z, 3, out=torch.zeros((3, 48), dtype=torch.uint8))
