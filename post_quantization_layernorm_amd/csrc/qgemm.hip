@@ -10,11 +10,15 @@
 //   Y[m][n] = s_w[n] * sum_c s_c * (acc_c[m][n] - z_c * colsum_c[n]),
 //   acc_c   = sum over the cluster's K-segment of q * W'   (int32, exact).
 //
-// Design (two 256-thread workgroups per CU, 4 waves each, so every SIMD runs
-// two waves whose VALU work overlaps the other's MFMAs, and one workgroup's
-// barrier waits are covered by the other's MFMAs):
-//   - 128 x 128 output tile, waves in a 2 x 2 grid of 64 x 64, each wave a
-//     2 x 2 grid of v_mfma_i32_32x32x32_i8 tiles;
+// Design (two workgroups per CU, so one workgroup's barrier waits are covered
+// by the other's MFMAs, and the waves of a SIMD overlap one another's VALU
+// work and MFMAs):
+//   - 128 x 128 output tile.  With 3- and 4-bit operands, 8 waves in a 2 x 4
+//     grid of 64 x 32 wave tiles (two v_mfma_i32_32x32x32_i8 tiles each):
+//     64 int32 + fp32 accumulator registers per lane leave room for four
+//     waves per SIMD (at most 128 VGPRs).  With an 8-bit operand the staging
+//     registers do not fit that, and 4 waves in a 2 x 2 grid of 64 x 64 (2 x 2
+//     MFMA tiles each) run two waves per SIMD;
 //   - K advances in stages of 128 codes (4 MFMA steps of 32).  Clusters are
 //     padded to multiples of 32 codes, so a step never straddles clusters;
 //   - A (3/4/8-bit activation codes) and W' (3/4/8-bit weights) are fetched
@@ -34,7 +38,8 @@
 //     weights as 16 * w (nibble moved to the high half of the byte, sign for
 //     free) and 3-bit weights as 32 * w; all are undone exactly: s_c / 16 or
 //     s_c / 32 in the scale, and
-//     corr[n] = sum_c s_c (z_c - offset) colsum_c[n] (fp64) in the epilogue;
+//     corr[n] = sum_c s_c (z_c - offset) colsum_c[n] (fp64, per column) in the
+//     epilogue, which writes Y = fma(s_w, out, -s_w corr) in fp32;
 //   - workgroups are numbered so that consecutive tiles of a group land on
 //     the same XCD (the dispatcher deals workgroups round-robin over the 8
 //     XCDs), sharing its L2.
@@ -120,16 +125,17 @@ __device__ __forceinline__ void store32(int8_t* lds, const uint32_t (&o)[8]) {
     reinterpret_cast<u32x4*>(lds)[1] = u32x4{o[4], o[5], o[6], o[7]};
 }
 
-// Tile configuration: BM x BN output tile, WAVES waves in a (BM/64) x (BN/64)
-// grid of 64 x 64 wave tiles, SK 32-code steps per pipeline stage, MINBLK
+// Tile configuration: BM x BN output tile, WAVES waves in a (BM/64) x WN grid
+// of 64 x (32 TJ) wave tiles, SK 32-code steps per pipeline stage, MINBLK
 // resident workgroups per CU.
-template <int BM_, int BN_, int WAVES_, int SK_, int MINBLK_>
+template <int BM_, int BN_, int WAVES_, int SK_, int MINBLK_, int TJ_ = 2>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WAVES = WAVES_, SK = SK_, MINBLK = MINBLK_;
-    static constexpr int NT = WAVES * 64, WN = BN / 64;
+    static constexpr int TJ = TJ_;                      // 32-column MFMA tiles per wave
+    static constexpr int NT = WAVES * 64, WN = BN / (32 * TJ);
     static constexpr int LDSS = SK * 32 + 16;          // LDS row stride (bytes)
     static constexpr int PA = BM * SK / NT, PB = BN * SK / NT;   // pieces per thread
-    static_assert((BM / 64) * (BN / 64) == WAVES, "one 64x64 tile per wave");
+    static_assert((BM / 64) * WN == WAVES, "one 64 x 32*TJ tile per wave");
     static_assert(PA * NT == BM * SK && PB * NT == BN * SK && PA >= 1 && PB >= 1, "staging split");
 };
 
@@ -146,7 +152,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     float* __restrict__ Y, int32_t* __restrict__ acc_dbg, int32_t tiles_m, int32_t tiles_n,
     const QuantOutArgs qo, const ClusterArgs qc) {
     constexpr int BM = CFG::BM, BN = CFG::BN, SK = CFG::SK, LDSS = CFG::LDSS, NT = CFG::NT;
-    constexpr int PA = CFG::PA, PB = CFG::PB, WN = CFG::WN;
+    constexpr int PA = CFG::PA, PB = CFG::PB, WN = CFG::WN, TJ = CFG::TJ, WW = 32 * TJ;
     constexpr int NPIECE = PA + PB;
     static_assert(NPIECE <= SK, "one staged piece per step");
     // both operands are unpacked to int8 on their way into LDS (once per
@@ -256,28 +262,28 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     // fp32 out.  With A_c the running sum at the end of cluster c,
     //   sum_c s_c (A_c - A_(c-1)) = sum_c (s_c - s_(c+1)) A_c,  s_(g+1) = 0,
     // so at each cluster end out += d_c * A_c and nothing is reset.
-    v16i acc[2][2];
-    float out[2][2][16];
+    v16i acc[2][TJ];
+    float out[2][TJ][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TJ; ++j) {
             acc[i][j] = (v16i)0;
 #pragma unroll
             for (int r = 0; r < 16; ++r) out[i][j][r] = 0.0f;
         }
-    [[maybe_unused]] v16i prev[2][2];
+    [[maybe_unused]] v16i prev[2][TJ];
     if constexpr (DEBUG) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) prev[i][j] = (v16i)0;
+            for (int j = 0; j < TJ; ++j) prev[i][j] = (v16i)0;
     }
 
     // accumulator register r of this lane holds row (r/4)*8 + (lane/32)*4 + r%4, column lane%32
     const int row_l = (lane >> 5) * 4, col_l = lane & 31;
     const int a_frag = (wm * 64 + (lane & 31)) * LDSS + (lane >> 5) * 16;
-    const int b_frag = (wn * 64 + (lane & 31)) * LDSS + (lane >> 5) * 16;
+    const int b_frag = (wn * WW + (lane & 31)) * LDSS + (lane >> 5) * 16;
 
     int c = 0, c_end = __builtin_amdgcn_readfirstlane(end_l);
 
@@ -286,12 +292,12 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < TJ; ++j) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     out[i][j][r] = __builtin_fmaf(d, (float)acc[i][j][r], out[i][j][r]);
                 if constexpr (DEBUG) {
-                    const int n = n0 + wn * 64 + j * 32 + col_l;
+                    const int n = n0 + wn * WW + j * 32 + col_l;
                     const int add = (n < N && ga.code_offset) ? ga.code_offset * colsum[(int64_t)cl * N + n] : 0;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -310,14 +316,14 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     // only registers and cover the latency of the next stage's first
     // fragment reads, which cannot be issued before it.  (Slot 1 starts at
     // zero, so the deferred MFMAs before stage 0 add nothing.)
-    v4i af[2][2], bf[2][2];
+    v4i af[2][2], bf[2][TJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i) af[1][i] = (v4i)0;
     auto mfmas = [&](int slot) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < TJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[slot][i], bf[slot][j], acc[i][j], 0, 0, 0);
     };
     auto flush_if_end = [&](int steps_done) {
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
             for (int i = 0; i < 2; ++i)
                 af[slot][i] = *reinterpret_cast<const v4i*>(&As[buf][a_frag + i * 32 * LDSS + ks * 32]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < TJ; ++j)
                 bf[slot][j] = *reinterpret_cast<const v4i*>(&Bs[buf][b_frag + j * 32 * LDSS + ks * 32]);
         };
         rd(0, 0);
@@ -359,6 +365,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
             // issue order inside the step: each MFMA is followed by part of
             // the next step's fragment reads, the unpack VALU work, and last
             // the staging stores (so the reads never wait behind them)
+            if constexpr (TJ == 2) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
@@ -370,6 +377,16 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            }
             if (ks + 1 < SK || last) flush_if_end(st * SK + ks + 1);
         }
     };
@@ -406,8 +423,8 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     if (quant) __syncthreads();                                 // every wave is done with the staging tiles
     const float qhi = kRoundMagic + (float)((1 << qc.bits) - 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + col_l;
+    for (int j = 0; j < TJ; ++j) {
+        const int n = n0 + wn * WW + j * 32 + col_l;
         if (n >= N) continue;
         double corr = 0.0;
         if (ga.dev_s) {
@@ -417,7 +434,9 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
         } else {
             for (int cc = 0; cc < ga.g; ++cc) corr += ga.sz[cc] * (double)colsum[(int64_t)cc * N + n];
         }
-        const double sw = (double)s_w[n];
+        // y = s_w (out - corr) as one fma: s_w * out exactly, plus the fp32
+        // rounding of -s_w * corr (formed in fp64)
+        const float swf = s_w[n], nswc = (float)(-(double)swf * corr);
         // the next layer's cluster of position n (pad positions: no cluster)
         float inv = 0.0f, zf = 0.0f;
         bool real = false;
@@ -434,11 +453,11 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
             for (int r = 0; r < 16; ++r) {
                 const int rl = wm * 64 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
                 const int64_t m = m0 + rl;
-                float y = (float)(sw * ((double)out[i][j][r] - corr));
+                float y = __builtin_fmaf(swf, out[i][j][r], nswc);
                 if (quant) {
                     if (qo.act) y = __builtin_fmaxf(y, 0.0f);
                     const uint32_t qb = quant_bits(y, inv, zf, qhi);
-                    ctile[rl * 128 + wn * 64 + j * 32 + col_l] = real ? (uint8_t)qb : 0;
+                    ctile[rl * 128 + wn * WW + j * 32 + col_l] = real ? (uint8_t)qb : 0;
                 }
                 if (Y && m < M) __builtin_nontemporal_store(y, Y + m * N + n);
             }
@@ -446,9 +465,11 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     if (quant) {
         __syncthreads();
         // 128 rows x 4 groups of 32 positions: two groups per thread
+        constexpr int GPT = BM * (BN / 32) / NT;            // 32-position groups per thread
+        static_assert(GPT * NT == BM * (BN / 32) && BN == 128, "code tile split");
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int gi = tid * 2 + k, rl = gi >> 2, grp = gi & 3;
+        for (int k = 0; k < GPT; ++k) {
+            const int gi = tid * GPT + k, rl = gi >> 2, grp = gi & 3;
             const int64_t m = m0 + rl;
             if (m >= M || n0 + grp * 32 >= N) continue;
             const u32x4 lo = *reinterpret_cast<const u32x4*>(ctile + rl * 128 + grp * 32);
@@ -479,12 +500,21 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     }
 }
 
-using Cfg = TileCfg<128, 128, 4, 4, 2>;
+using CfgNarrow = TileCfg<128, 128, 8, 4, 2, 1>;      // 3/4-bit operands: 64 x 32 wave tiles
+using CfgWide = TileCfg<128, 128, 4, 4, 2, 2>;        // an 8-bit operand: 64 x 64 wave tiles
+static_assert(CfgNarrow::BM == CfgWide::BM && CfgNarrow::BN == CfgWide::BN, "one tile grid");
+using Cfg = CfgWide;
+
+template <int ABITS, int WBITS>
+using CfgFor = std::conditional_t<(ABITS <= 4 && WBITS <= 4), CfgNarrow, CfgWide>;
 
 template <int ABITS, int WBITS>
 const void* pick2(bool debug) {
-    return debug ? (const void*)qgemm_kernel<ABITS, WBITS, true, Cfg> : (const void*)qgemm_kernel<ABITS, WBITS, false, Cfg>;
+    using C = CfgFor<ABITS, WBITS>;
+    return debug ? (const void*)qgemm_kernel<ABITS, WBITS, true, C> : (const void*)qgemm_kernel<ABITS, WBITS, false, C>;
 }
+
+int threads_for(int a_bits, int w_bits) { return a_bits <= 4 && w_bits <= 4 ? CfgNarrow::NT : CfgWide::NT; }
 
 template <int ABITS>
 const void* pick(int wbits, bool debug) {
@@ -507,7 +537,7 @@ hipError_t launch_qgemm(const uint8_t* codes, int64_t M, int32_t N, int64_t a_ro
     void* args[] = {(void*)&codes, (void*)&M, (void*)&arb, (void*)&w_packed, (void*)&N, (void*)&wrb,
                     (void*)&ga, (void*)&s_w, (void*)&colsum, (void*)&Y, (void*)&acc_debug,
                     (void*)&tiles_m, (void*)&tiles_n, (void*)&qo, (void*)&qc};
-    return hipLaunchKernel(k, dim3((unsigned)(tm * tn)), dim3(Cfg::NT), args, 0, stream);
+    return hipLaunchKernel(k, dim3((unsigned)(tm * tn)), dim3(threads_for(a_bits, w_bits)), args, 0, stream);
 }
 
 }  // namespace rptq
