@@ -49,8 +49,12 @@
  *     that size rounded up to a multiple of 64 bytes (rptq_codes_row_bytes),
  *     so that the GEMM's 64-byte stage segments of a row never straddle two
  *     64-byte memory sectors.  The bytes between the codes and the pitch are
- *     neither written by the producers nor read by the GEMM.  Packed weights
- *     use the same pitch (rptq_weights_row_bytes), with those bytes zero.
+ *     not written by the producers; the GEMM may read them (and the first
+ *     bytes of the next row) when K ends inside one of its 128-code stages,
+ *     and takes their products with zero weights, so any values there are
+ *     harmless.  Packed weights use the same pitch (rptq_weights_row_bytes),
+ *     and the bytes between a row's weights and its pitch must be zero (the
+ *     weight packers write them so).
  *
  * Conventions for every entry point.
  *   - Pointers marked "device" are GPU memory owned by the caller (for

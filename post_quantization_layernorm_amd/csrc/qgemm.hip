@@ -227,19 +227,32 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     // memory-counter waits at the loop head conservative
     const int nst = ((nsteps + SK - 1) / SK + 1) & ~1;
 
-    // Pieces of steps past the end of K read as zero (offset beyond the
-    // buffer), so the MFMAs of a partial last stage add nothing.
     using Stage = StageRegs<ABITS, WBITS, PA, PB>;
-    // piece k (A pieces first, then W' pieces) of stage st into register set S
+    // Bytes from the tile's first row to the end of each operand, clamped to
+    // 31 bits once, so that each stage's buffer size is scalar 32-bit
+    // arithmetic (a 64-bit clamp per load would take vector compares).
+    const int32_t a_left32 = __builtin_amdgcn_readfirstlane((int32_t)(a_left < 0 ? 0 : a_left > 0x7fffffff ? 0x7fffffff : a_left));
+    const int32_t b_left32 = __builtin_amdgcn_readfirstlane((int32_t)(b_left < 0 ? 0 : b_left > 0x7fffffff ? 0x7fffffff : b_left));
+    // piece k (A pieces first, then W' pieces) of stage st into register set S.
+    // Stages past the end of K get an empty buffer (every load reads zero).
+    // In the last stage, the steps past K: with 4-bit weights the W' row pitch
+    // (64 bytes = 128 codes) covers whole stages and its tail is zero (the
+    // weight packer writes it), so those steps read zero weights against
+    // whatever codes follow the row and need no per-lane test; other widths
+    // send those lanes' loads out of range.
+    constexpr bool kStepTest = WBITS != 4;
     auto gload_piece = [&](Stage& S, int st, int k) {
         const int room = nsteps - st * SK;
         if (k < PA) {
-            const int64_t ao = (int64_t)st * (SK * APIECE);
-            load_piece<ABITS>(make_rsrc(a_tile + ao, a_left - ao), a_step[k] < room ? a_voff[k] : 0x80000000u, S.a[k]);
+            const int32_t ao = st * (SK * APIECE);
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(a_tile) + ao, (short)0, room > 0 ? max(a_left32 - ao, 0) : 0, kRsrcWord3);
+            load_piece<ABITS>(r, !kStepTest || a_step[k] < room ? a_voff[k] : 0x80000000u, S.a[k]);
         } else {
-            const int64_t bo = (int64_t)st * (SK * BPIECE);
-            load_piece<WBITS>(make_rsrc(b_tile + bo, b_left - bo), b_step[k - PA] < room ? b_voff[k - PA] : 0x80000000u,
-                              S.b[k - PA]);
+            const int32_t bo = st * (SK * BPIECE);
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(b_tile) + bo, (short)0, room > 0 ? max(b_left32 - bo, 0) : 0, kRsrcWord3);
+            load_piece<WBITS>(r, !kStepTest || b_step[k - PA] < room ? b_voff[k - PA] : 0x80000000u, S.b[k - PA]);
         }
     };
     auto gload = [&](Stage& S, int st) {
