@@ -375,9 +375,11 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
                 put(nxt, buf ^ 1, ks);                  // unused on the last stage
                 gload_piece(nxt, st + 3, ks);           // that piece is free again: reload it two stages ahead
             }
-            // issue order inside the step: each MFMA is followed by part of
-            // the next step's fragment reads, the unpack VALU work, and last
-            // the staging stores (so the reads never wait behind them)
+            // issue order inside the step (64 x 64 wave tiles; with 64 x 32
+            // tiles the compiler's own order is as fast): each MFMA is
+            // followed by part of the next step's fragment reads, the unpack
+            // VALU work, and last the staging stores (so the reads never wait
+            // behind them)
             if constexpr (TJ == 2) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
@@ -389,15 +391,6 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-            } else {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
             }
             if (ks + 1 < SK || last) flush_if_end(st * SK + ks + 1);
@@ -435,6 +428,11 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     uint8_t* ctile = reinterpret_cast<uint8_t*>(&As[0][0]);     // 128 x 128 codes
     if (quant) __syncthreads();                                 // every wave is done with the staging tiles
     const float qhi = kRoundMagic + (float)((1 << qc.bits) - 1);
+    // Y of this tile through one buffer resource: rows past M lie outside it
+    // (those stores are dropped), so an element needs only its 32-bit byte
+    // offset (a tile spans at most BM * N * 4 < 2^31 bytes, checked at launch)
+    const __amdgpu_buffer_rsrc_t ry =
+        make_rsrc(Y ? Y + m0 * N : nullptr, Y ? min(M - m0, (int64_t)BM) * N * 4 : 0);
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
         const int n = n0 + wn * WW + j * 32 + col_l;
@@ -460,19 +458,24 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
                     inv = qc.inv_s[cc];
                     zf = (float)qc.z[cc];
                 }
+        uint32_t ybase = ((uint32_t)(wm * 64 + row_l) * (uint32_t)N + (uint32_t)n) * 4u;
+        asm volatile("" : "+v"(ybase));         // keep one base + a scalar row offset per element
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int rl = wm * 64 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
-                const int64_t m = m0 + rl;
+                const int dr = i * 32 + (r >> 2) * 8 + (r & 3);      // row within the wave tile
+                const int rl = wm * 64 + dr + row_l;
                 float y = __builtin_fmaf(swf, out[i][j][r], nswc);
                 if (quant) {
                     if (qo.act) y = __builtin_fmaxf(y, 0.0f);
                     const uint32_t qb = quant_bits(y, inv, zf, qhi);
                     ctile[rl * 128 + wn * WW + j * 32 + col_l] = real ? (uint8_t)qb : 0;
                 }
-                if (Y && m < M) __builtin_nontemporal_store(y, Y + m * N + n);
+                if (Y)
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __builtin_bit_cast(uint32_t, y), ry,
+                        ybase + (uint32_t)__builtin_amdgcn_readfirstlane(dr * N * 4), 0, kStreamPolicy);
             }
     }
     if (quant) {
@@ -544,7 +547,9 @@ hipError_t launch_qgemm(const uint8_t* codes, int64_t M, int32_t N, int64_t a_ro
     const bool dbg = acc_debug != nullptr;
     const void* k = a_bits == 3 ? pick<3>(w_bits, dbg) : a_bits == 4 ? pick<4>(w_bits, dbg) : pick<8>(w_bits, dbg);
     const int64_t tm = (M + Cfg::BM - 1) / Cfg::BM, tn = (N + Cfg::BN - 1) / Cfg::BN;
-    if (tm * tn > 0x7fffffff || a_row_bytes > (1 << 20) || w_row_bytes > (1 << 20)) return hipErrorInvalidValue;
+    if (tm * tn > 0x7fffffff || a_row_bytes > (1 << 20) || w_row_bytes > (1 << 20) ||
+        (int64_t)N * 4 * std::max(CfgNarrow::BM, CfgWide::BM) > 0x7fffffff)
+        return hipErrorInvalidValue;
     int32_t tiles_m = (int32_t)tm, tiles_n = (int32_t)tn;
     int32_t arb = (int32_t)a_row_bytes, wrb = (int32_t)w_row_bytes;
     void* args[] = {(void*)&codes, (void*)&M, (void*)&arb, (void*)&w_packed, (void*)&N, (void*)&wrb,
