@@ -304,6 +304,36 @@ def test_qgemm_many_tiles_bit_exact(P, case):
     assert torch.equal(Y, Y2)
 
 
+# With 4-bit weights the GEMM reads the codes of its last, partial 128-code
+# stage past K (the row's pitch tail, and for 8-bit codes here also the
+# first bytes of the next row) against the zero tail of the weight rows: any
+# values there leave every accumulator and Y unchanged.
+@pytest.mark.parametrize("case", [(200, 2048, 392, 8, 4, 4), (64, 9216, 136, 32, 3, 4), (33, 9216, 128, 32, 8, 4)],
+                         ids=lambda c: "M{}K{}N{}g{}A{}W{}".format(*c))
+def test_qgemm_ignores_code_bytes_past_k(P, case):
+    M, K, N, g, ab, wb = case
+    _say("gemm code bytes past K", case)
+    c = layer_case(M, K, N, g, ab, wb, seed=M + 7)
+    kp = orc.seg32_kpad(c.bounds)
+    assert (kp // 32) % 4 != 0              # a partial last stage
+    q, codes = _oracle_codes(c)
+    Y_o, acc_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w, return_acc=True)
+    wp, cs, sw = _gemm_inputs(P, c)
+    clean = pitched(codes, c.bounds, ab)
+    dirty = clean.copy()
+    dirty[:, codes.shape[1]:] = 0xA5        # the pitch tail the producers leave unwritten
+    out = []
+    for a in (clean, dirty):
+        acc = torch.full((g, M, N), -7, dtype=torch.int32, device="cuda")
+        Y = P.rptq_qgemm(dev(a), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs, acc_debug=acc)
+        torch.cuda.synchronize()
+        assert np.array_equal(acc.cpu().numpy(), acc_o)
+        out.append(P.rptq_qgemm(dev(a), M, K, N, c.bounds, c.s, c.z, ab, wp, wb, sw, cs))
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], out[1])
+    assert rel_l2(out[1].cpu().numpy(), Y_o) <= 1e-3
+
+
 @pytest.mark.parametrize("bounds", [[0, 1, 2, 3, 64, 96, 97, 160, 256], [0, 256],
                                     list(range(0, 65)) + [256]],
                          ids=["size1", "g1", "g65"])
