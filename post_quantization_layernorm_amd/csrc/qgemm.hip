@@ -15,8 +15,8 @@
 // work and MFMAs):
 //   - 128 x 128 output tile.  With 3- and 4-bit operands, 8 waves in a 2 x 4
 //     grid of 64 x 32 wave tiles (two v_mfma_i32_32x32x32_i8 tiles each):
-//     64 int32 + fp32 accumulator registers per lane leave room for four
-//     waves per SIMD (at most 128 VGPRs).  With an 8-bit operand the staging
+//     32 int32 and 32 fp32 accumulator registers per lane leave room for
+//     four waves per SIMD (at most 128 VGPRs).  With an 8-bit operand the staging
 //     registers do not fit that, and 4 waves in a 2 x 2 grid of 64 x 64 (2 x 2
 //     MFMA tiles each) run two waves per SIMD;
 //   - K advances in stages of 128 codes (4 MFMA steps of 32).  Clusters are
