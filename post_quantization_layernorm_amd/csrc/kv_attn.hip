@@ -5,13 +5,14 @@
 // sequence length they hold most of the memory.  Attention then has to read
 // them back; instead of a separate dequantize pass that writes the fp16
 // cache to HBM and an attention pass that reads it again, every packed row
-// is decoded on its way into LDS and consumed there.  The decode writes
-// each code's exact (q - z_c) as an fp16 integer, scattered back to natural
-// channel order (1024 + q is formed from the code bits, and one packed fp16
-// add of -(1024 + z_c) per pair of codes leaves q - z_c exactly); the
-// cluster scale s_c is applied in fp32 outside the per-row work: folded into
-// the query for the scores (q_c * s_c), and into each output channel of the
-// value sums at the end.  So the cache values enter the arithmetic as
+// is decoded on its way through LDS and consumed there.  The decode forms
+// each code's exact (q - z_c) as an fp16 integer (1024 + q is formed from
+// the code bits, and one packed fp16 add of -(1024 + z_c) per pair of codes
+// leaves q - z_c exactly); for the keys it is scattered back to natural
+// channel order, the values are summed in code order.  The cluster scale
+// s_c is applied in fp32 outside the per-row work: folded into the query
+// for the scores (q_c * s_c), and into each output channel of the value
+// sums at the end.  So the cache values enter the arithmetic as
 // s_c (q - z_c) without the fp16 rounding of the standalone dequantize (a
 // difference of at most half an fp16 ulp per value).
 //
@@ -23,8 +24,10 @@
 //      channels (fp32 q_c * s_c against the fp16 (q - z_c)), reduced with
 //      lane shuffles: S[t][h] = scale * q_h . k_h;
 //   2. softmax inside the chunk: m_h = max_t S, p = exp(S - m_h), l_h = sum p;
-//   3. values: every lane owns 8-channel slices of the output and adds
-//      p[t][h] * v over the chunk's value rows.
+//   3. values: every lane keeps, for the codes of its units, the sum of
+//      p[t][head] * (q - z) over the chunk's value rows in registers (no
+//      scatter, one barrier per row) and stores it to the codes' natural
+//      channels at the end.
 // A second kernel merges the chunks of a sequence: with M = max_k m_k,
 //   out = sum_k e^(m_k - M) o_k / sum_k e^(m_k - M) l_k.
 #include "rptq_device.hpp"
@@ -264,42 +267,93 @@ __global__ __launch_bounds__(kAttnBlock) void kv_attn_chunk_kernel(
     }
     __syncthreads();
 
-    // ---- 3. values: lane owns output slices oc = tid + 256 u (8 channels)
+    // ---- 3. values, in code order: each lane keeps, for the codes of its
+    // units, the sum over the chunk's rows of p[t][head] * (q - z) in
+    // registers (a channel's sum runs over the rows in the same order as a
+    // natural-order pass would), and stores it to the channel's natural place
+    // once at the end: no per-row scatter, one barrier per row.
     float acc[UPL][8];
-#pragma unroll
-    for (int u = 0; u < UPL; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
+    int hd[UPL][8];                                           // head of each code
     tables(tv);
-    run_rows(vp, [&](int t) {
 #pragma unroll
-        for (int u = 0; u < UPL; ++u) {
-            const int oc = tid + u * kAttnBlock;
-            if (oc < n_units) {
-                const u32x4 x = *reinterpret_cast<const u32x4*>(xrow + oc * 16);
-                const float p = S[t * H + oc * 8 / D];
-                const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+    for (int u = 0; u < UPL; ++u) {
+        const bool live = tid + u * kAttnBlock < n_units;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const half2_t hv = __builtin_bit_cast(half2_t, xs[w]);
-                    acc[u][2 * w] = __builtin_fmaf(p, (float)hv.x, acc[u][2 * w]);
-                    acc[u][2 * w + 1] = __builtin_fmaf(p, (float)hv.y, acc[u][2 * w + 1]);
+        for (int e = 0; e < 8; ++e) {
+            acc[u][e] = 0.0f;
+            hd[u][e] = live ? (dst[u][e] >> 1) / D : 0;
+        }
+    }
+    {
+        const uint8_t* rows = vp + ((int64_t)b * T + t0) * row_bytes;
+        wait_vm<0>();                                         // nothing older in the count
+        __syncthreads();                                      // the ring is free
+#pragma unroll
+        for (int p = 0; p < kAttnRing - 1; ++p) issue_row(rows, p);
+        for (int t = 0; t < nv; ++t) {
+            wait_vm<(kAttnRing - 2) * CH>();                  // this wave's part of row t is in LDS
+            lds_barrier();                                    // every part; every wave done with row t - 1
+            issue_row(rows, t + kAttnRing - 1);               // into the slot of row t - 1
+            const unsigned char* prow = ring + (size_t)(t % kAttnRing) * SLOT;
+            const float* St = S + t * H;
+            uint32_t raw[UPL][BITS == 8 ? 2 : BITS == 4 ? 1 : 3];
+#pragma unroll
+            for (int u = 0; u < UPL; ++u) {
+                const unsigned char* pu = prow + uib[u];
+                if constexpr (BITS == 8) {
+                    const uint2 v = *reinterpret_cast<const uint2*>(pu);
+                    raw[u][0] = v.x; raw[u][1] = v.y;
+                } else if constexpr (BITS == 4) {
+                    raw[u][0] = *reinterpret_cast<const uint32_t*>(pu);
+                } else {
+                    raw[u][0] = pu[0]; raw[u][1] = pu[4]; raw[u][2] = pu[8];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UPL; ++u) {
+                int qv[8];
+                if constexpr (BITS == 8) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        qv[i] = (raw[u][0] >> (8 * i)) & 255;
+                        qv[4 + i] = (raw[u][1] >> (8 * i)) & 255;
+                    }
+                } else if constexpr (BITS == 4) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        qv[i] = (raw[u][0] >> (8 * i)) & 15;
+                        qv[4 + i] = (raw[u][0] >> (8 * i + 4)) & 15;
+                    }
+                } else {
+                    const int b0 = raw[u][0], b1 = raw[u][1], b2 = raw[u][2];
+                    qv[0] = b0 & 7; qv[1] = (b0 >> 3) & 7;
+                    qv[2] = b1 & 7; qv[3] = (b1 >> 3) & 7;
+                    qv[4] = b2 & 7; qv[5] = (b2 >> 3) & 7;
+                    qv[6] = (b0 >> 6) | ((b2 >> 6) & 1) << 2;
+                    qv[7] = (b1 >> 6) | ((b2 >> 7) & 1) << 2;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t w = (uint32_t)qv[2 * i] | (uint32_t)qv[2 * i + 1] << 16 | 0x64006400u;
+                    const half2_t hv = __builtin_bit_cast(half2_t, w) + nz[u][i];      // q - z, exact
+                    acc[u][2 * i] = __builtin_fmaf(St[hd[u][2 * i]], (float)hv.x, acc[u][2 * i]);
+                    acc[u][2 * i + 1] = __builtin_fmaf(St[hd[u][2 * i + 1]], (float)hv.y, acc[u][2 * i + 1]);
                 }
             }
         }
-    });
-    // each output channel's sum of p (q - z) times its value cluster's s
+        wait_vm<0>();
+    }
+    // each channel's sum of p (q - z) times its value cluster's s, to its
+    // natural place
     float* op = o_part + ((int64_t)b * nch + kc) * C;
 #pragma unroll
     for (int u = 0; u < UPL; ++u) {
-        const int oc = tid + u * kAttnBlock;
-        if (oc < n_units) {
-            const float4 s0 = reinterpret_cast<const float4*>(tv.s + oc * 8)[0];
-            const float4 s1 = reinterpret_cast<const float4*>(tv.s + oc * 8)[1];
-            reinterpret_cast<float4*>(op + oc * 8)[0] =
-                float4{acc[u][0] * s0.x, acc[u][1] * s0.y, acc[u][2] * s0.z, acc[u][3] * s0.w};
-            reinterpret_cast<float4*>(op + oc * 8)[1] =
-                float4{acc[u][4] * s1.x, acc[u][5] * s1.y, acc[u][6] * s1.z, acc[u][7] * s1.w};
+        if (tid + u * kAttnBlock < n_units) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int chn = dst[u][e] >> 1;
+                op[chn] = acc[u][e] * tv.s[chn];
+            }
         }
     }
 }
