@@ -89,6 +89,7 @@ typedef enum {
 
 #define RPTQ_MAX_CLUSTERS 64
 #define RPTQ_MAX_K 16384
+#define RPTQ_MAX_GEMM_N 4194303  /* a 128-row tile of fp32 Y spans N * 512 bytes < 2^31 */
 #define RPTQ_MAX_ABS_ZERO_POINT (1 << 21)
 
 enum {
@@ -147,7 +148,8 @@ int rptq_ln_reorder_quant(const void* x, int32_t in_mode, int64_t M, int32_t K,
  * Y        device fp32 [M][N], row-major.
  * acc_debug device int32 [g][M][N] or NULL: receives every acc_c (validation).
  * Limits: K <= RPTQ_MAX_K (RPTQ_ERR_UNSUPPORTED), which also keeps every
- * |acc_c| within int32; any M >= 0 and N >= 1.
+ * |acc_c| within int32; 1 <= N <= RPTQ_MAX_GEMM_N (RPTQ_ERR_UNSUPPORTED
+ * above); any M >= 0.
  */
 int rptq_qgemm(const uint8_t* codes, int64_t M, int32_t K, int32_t N,
                const int32_t* bounds, int32_t g, const float* s, const int32_t* z, int32_t a_bits,

@@ -547,8 +547,8 @@ hipError_t launch_qgemm(const uint8_t* codes, int64_t M, int32_t N, int64_t a_ro
     const bool dbg = acc_debug != nullptr;
     const void* k = a_bits == 3 ? pick<3>(w_bits, dbg) : a_bits == 4 ? pick<4>(w_bits, dbg) : pick<8>(w_bits, dbg);
     const int64_t tm = (M + Cfg::BM - 1) / Cfg::BM, tn = (N + Cfg::BN - 1) / Cfg::BN;
-    if (tm * tn > 0x7fffffff || a_row_bytes > (1 << 20) || w_row_bytes > (1 << 20) ||
-        (int64_t)N * 4 * std::max(CfgNarrow::BM, CfgWide::BM) > 0x7fffffff)
+    static_assert((int64_t)kMaxGemmN * 4 * std::max(CfgNarrow::BM, CfgWide::BM) <= 0x7fffffff, "Y tile window");
+    if (tm * tn > 0x7fffffff || a_row_bytes > (1 << 20) || w_row_bytes > (1 << 20) || N > kMaxGemmN)
         return hipErrorInvalidValue;
     int32_t tiles_m = (int32_t)tm, tiles_n = (int32_t)tn;
     int32_t arb = (int32_t)a_row_bytes, wrb = (int32_t)w_row_bytes;

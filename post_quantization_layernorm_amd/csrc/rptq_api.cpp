@@ -297,6 +297,8 @@ static int qgemm_common(const uint8_t* codes, int64_t M, int32_t K, int32_t N, c
         return st;
     }
     if (K > kMaxK) return fail(RPTQ_ERR_UNSUPPORTED, "K = %d exceeds %d", K, kMaxK);
+    static_assert(kMaxGemmN == RPTQ_MAX_GEMM_N, "header limit");
+    if (N > kMaxGemmN) return fail(RPTQ_ERR_UNSUPPORTED, "N = %d exceeds %d", N, kMaxGemmN);
     if (M == 0) return ok();
     if (!codes || !w_packed || !s_w || !colsum || (!Y && !qo.q_codes))
         return fail(RPTQ_ERR_INVALID_ARG, "codes, w_packed, s_w, colsum and the output must be non-NULL");

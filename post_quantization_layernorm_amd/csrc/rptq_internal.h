@@ -9,6 +9,7 @@ namespace rptq {
 
 constexpr int kMaxClusters = 64;
 constexpr int kMaxK = 16384;
+constexpr int kMaxGemmN = 4194303;     // GEMM N: 128 rows x N fp32 of a Y tile < 2^31 bytes
 constexpr int kMaxBlock = 512;         // largest workgroup of the streaming kernels
 constexpr int kKvPackMaxBlock = 1024;  // K/V pack: one wide workgroup per compute unit
 constexpr int kMaxUpl = 5;             // most units (8 codes each) one lane handles

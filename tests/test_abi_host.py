@@ -158,6 +158,7 @@ def _gemm(P, **kw):
     (dict(K=63), -1), (dict(s=np.array([0.1, -0.2], np.float32)), -1), (dict(w=None), -1),
     (dict(colsum=None), -1), (dict(Y=None), -1), (dict(s_w=None), -1),
     (dict(K=16392, bounds=np.array([0, 8, 16392], np.int32)), -2),
+    (dict(N=4194304), -2),
     (dict(codes=MISALIGNED), -3), (dict(Y=MISALIGNED), -3), (dict(acc=MISALIGNED), -3),
 ])
 def test_qgemm_rejects(P, kw, status):
