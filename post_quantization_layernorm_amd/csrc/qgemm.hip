@@ -433,17 +433,31 @@ __global__ __launch_bounds__(CFG::NT, CFG::MINBLK) void qgemm_kernel(
     // offset (a tile spans at most BM * N * 4 < 2^31 bytes, checked at launch)
     const __amdgpu_buffer_rsrc_t ry =
         make_rsrc(Y ? Y + m0 * N : nullptr, Y ? min(M - m0, (int64_t)BM) * N * 4 : 0);
+    // colsum [g][N]: at most 64 x 4194303 int32, under 2^31 bytes
+    const __amdgpu_buffer_rsrc_t rcs = make_rsrc(colsum, (int64_t)ga.g * N * 4);
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
         const int n = n0 + wn * WW + j * 32 + col_l;
         if (n >= N) continue;
+        // colsum[c][n] of every cluster, 16 loads in flight at a time (one
+        // wait per 16 clusters, not one per cluster), then summed in cluster
+        // order; clusters past g read as zero through the buffer's range
         double corr = 0.0;
-        if (ga.dev_s) {
-            for (int cc = 0; cc < ga.g; ++cc)
-                corr += (double)ga.dev_s[cc] * ((double)ga.dev_z[cc] - (double)ga.code_offset) *
-                        (double)colsum[(int64_t)cc * N + n];
-        } else {
-            for (int cc = 0; cc < ga.g; ++cc) corr += ga.sz[cc] * (double)colsum[(int64_t)cc * N + n];
+        for (int c0 = 0; c0 < ga.g; c0 += 16) {
+            int32_t cs[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                cs[k] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                    rcs, c0 + k < ga.g ? (uint32_t)(((c0 + k) * N + n) * 4) : 0x80000000u, 0, 0);
+            if (ga.dev_s) {
+                for (int k = 0; k < 16 && c0 + k < ga.g; ++k)
+                    corr += (double)ga.dev_s[c0 + k] * ((double)ga.dev_z[c0 + k] - (double)ga.code_offset) *
+                            (double)cs[k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    if (c0 + k < ga.g) corr += ga.sz[c0 + k] * (double)cs[k];
+            }
         }
         // y = s_w (out - corr) as one fma: s_w * out exactly, plus the fp32
         // rounding of -s_w * corr (formed in fp64)
