@@ -211,14 +211,14 @@ def test_ln_dynamic_fused_within_tolerance(P, bits, shape):
     assert d.max() <= 1 and (d > 0).mean() <= 1e-3, (d.max(), (d > 0).mean())
 
 
-@pytest.mark.parametrize("ab,wb", [(4, 4), (3, 3), (8, 8), (8, 4), (3, 4)])
-def test_qgemm_dynamic(P, ab, wb):
+@pytest.mark.parametrize("ab,wb,g", [(4, 4, 8), (3, 3, 8), (8, 8, 8), (8, 4, 8), (3, 4, 8), (4, 4, 20)])
+def test_qgemm_dynamic(P, ab, wb, g):
     """The GEMM reading (s, z) from device memory: Y equals rptq_qgemm's with
     the same (s, z) passed from the host, bit for bit, and the oracle's GEMM
     of the kernel's codes within 1e-3."""
-    M, K, N, g = 150, 2048, 520, 8
+    M, K, N = 150, 2048, 520
     _say("gemm dynamic", ab, wb)
-    c = layer_case(M, K, N, g, ab, wb, seed=900 + ab + wb)
+    c = layer_case(M, K, N, g, ab, wb, seed=900 + ab + wb + g)
     gr, br = c.gamma[c.R], c.beta[c.R]
     codes, sd, zd = P.rptq_ln_reorder_quant_dynamic(dev(c.x.view(np.int16)).view(torch.float16), dev(c.R),
                                                     dev(gr), dev(br), c.bounds, ab)
@@ -260,6 +260,8 @@ GEMM_CASES = [  # (M, K, N, g, a_bits, w_bits)
     (3, 768, 1, 2, 8, 8),               # N = 1
     (130, 40, 33, 2, 3, 3),             # K = 40 (two clusters padded to 64 codes), odd N
     (1300, 512, 520, 4, 4, 4),          # 11 x 5 tiles: a partial last group of the grouped tile walk
+    (150, 2560, 264, 20, 4, 4),         # g = 20 and g = 37: the epilogue's colsum loads in batches of
+    (70, 4096, 136, 37, 3, 4),          # 16 clusters end with a partial batch
 ]
 
 
