@@ -262,6 +262,7 @@ GEMM_CASES = [  # (M, K, N, g, a_bits, w_bits)
     (1300, 512, 520, 4, 4, 4),          # 11 x 5 tiles: a partial last group of the grouped tile walk
     (150, 2560, 264, 20, 4, 4),         # g = 20 and g = 37: the epilogue's colsum loads in batches of
     (70, 4096, 136, 37, 3, 4),          # 16 clusters end with a partial batch
+    (100, 2560, 200, 20, 8, 8),         # (the 8-bit operand tile configuration too)
 ]
 
 
@@ -367,16 +368,16 @@ def test_end_to_end_ln_then_gemm(P, ab, wb):
 
 
 # ----------------------------------------------------------------------------- GEMM with quantized output
-@pytest.mark.parametrize("ab,wb,ob,act,N", [(4, 4, 4, 1, 330), (3, 3, 3, 1, 200), (8, 4, 8, 0, 130),
-                                             (4, 4, 3, 1, 1024)])
-def test_qgemm_quant_output(P, ab, wb, ob, act, N):
+@pytest.mark.parametrize("ab,wb,ob,act,N,g", [(4, 4, 4, 1, 330, 8), (3, 3, 3, 1, 200, 8), (8, 4, 8, 0, 130, 8),
+                                               (4, 4, 3, 1, 1024, 8), (4, 4, 4, 1, 330, 20)])
+def test_qgemm_quant_output(P, ab, wb, ob, act, N, g):
     """The epilogue quantizes the (activated) output for the next layer: the
     codes equal the oracle's quantization of the kernel's own y bit for bit,
     y matches the oracle's GEMM, and against the oracle end to end at most
     0.1% of the codes differ, by 1."""
-    M, K, g, g2 = 150, 2048, 8, 6
-    _say("gemm quant-out", ab, wb, ob, act, N)
-    c = layer_case(M, K, N, g, ab, wb, seed=500 + N + ab)
+    M, K, g2 = 150, 2048, 6
+    _say("gemm quant-out", ab, wb, ob, act, N, g)
+    c = layer_case(M, K, N, g, ab, wb, seed=500 + N + ab + g)
     q, codes = _oracle_codes(c)
     Y_o = orc.qgemm(q, c.Wq, c.R, c.bounds, c.s, c.z, c.s_w)
     a_o = np.maximum(Y_o, np.float32(0)) if act else Y_o
