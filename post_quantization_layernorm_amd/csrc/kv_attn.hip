@@ -367,9 +367,13 @@ __global__ __launch_bounds__(256) void kv_attn_combine_kernel(const float* __res
     if (c >= C) return;
     const int H = C / D, h = c / D;
     const float* mlb = ml + (int64_t)b * nch * H * 2;
+    // (both loops unrolled so that their loads are in flight together; the
+    // sums keep chunk order)
     float M = -__builtin_inff();
+#pragma unroll 16
     for (int k = 0; k < nch; ++k) M = __builtin_fmaxf(M, mlb[((int64_t)k * H + h) * 2]);
     float o = 0.0f, L = 0.0f;
+#pragma unroll 16
     for (int k = 0; k < nch; ++k) {
         const float w = __expf(mlb[((int64_t)k * H + h) * 2] - M);
         o = __builtin_fmaf(w, o_part[((int64_t)b * nch + k) * C + c], o);
